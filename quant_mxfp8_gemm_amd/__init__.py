@@ -1,0 +1,183 @@
+"""MI355X (gfx950) MXFP8 quantiser, fused Gemma RMSNorm quantiser and block-scaled GEMM.
+
+A thin ctypes binding over ``libmxfp8_amd.so`` (C ABI: ``include/mxfp8.h``). Every step of
+the computation runs in the library's HIP kernels; this module only checks tensor
+placement, allocates outputs with torch and passes raw device pointers together with
+torch's current HIP stream. There is no CPU fallback: without the built library (or
+without a GPU) every call raises.
+
+Data conventions (vLLM PR #64659 "Details: GEMM-RS with a quantized input", PR #65496
+"Details"): E4M3 data travels as ``torch.uint8`` tensors, UE8M0 scales as ``torch.uint8``
+(linear ``[rows, k/32]`` or the flat 128x4-swizzled buffer), BF16 as ``torch.bfloat16``.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxfp8_amd.so")
+
+LINEAR = 0
+SWIZZLED = 1
+
+OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4
+
+_lib = None
+
+
+class MXFP8Error(RuntimeError):
+    """A call into libmxfp8_amd returned a non-zero status."""
+
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+
+
+def load_library():
+    """Load libmxfp8_amd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m quant_mxfp8_gemm_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    lib.mxfp8_scale_bytes.restype = i64
+    lib.mxfp8_scale_bytes.argtypes = [i64, i64, i32]
+    lib.mxfp8_status_string.restype = ctypes.c_char_p
+    lib.mxfp8_status_string.argtypes = [i32]
+    lib.mxfp8_quantize.restype = i32
+    lib.mxfp8_quantize.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
+    lib.mxfp8_quantize_check.restype = i32
+    lib.mxfp8_quantize_check.argtypes = [vp, i64, i64, i64, vp, vp, vp]
+    lib.rmsnorm_quant_mxfp8.restype = i32
+    lib.rmsnorm_quant_mxfp8.argtypes = [vp, vp, i64, i64, i64, f32, vp, vp, vp, vp]
+    lib.rmsnorm_quant_mxfp8_check.restype = i32
+    lib.rmsnorm_quant_mxfp8_check.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
+    lib.mxfp8_gemm_bf16out.restype = i32
+    lib.mxfp8_gemm_bf16out.argtypes = [vp, vp, i32, vp, vp, i32, i64, i64, i64, vp, i64, i32, i32, vp, vp]
+    lib.mxfp8_gemm_bf16out_check.restype = i32
+    lib.mxfp8_gemm_bf16out_check.argtypes = [vp, vp, i32, vp, vp, i32, i64, i64, i64, vp, i64, i32, i32]
+    lib.mxfp8_gemm_tiles_per_chunk.restype = i64
+    lib.mxfp8_gemm_tiles_per_chunk.argtypes = [i64, i64, i32]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().mxfp8_status_string(int(status)).decode()
+
+
+def scale_bytes(rows: int, k: int, layout: int) -> int:
+    n = load_library().mxfp8_scale_bytes(int(rows), int(k), int(layout))
+    if n < 0:
+        raise MXFP8Error("mxfp8_scale_bytes", EINVAL)
+    return n
+
+
+def gemm_tiles_per_chunk(m: int, n: int, num_chunks: int) -> int:
+    t = load_library().mxfp8_gemm_tiles_per_chunk(int(m), int(n), int(num_chunks))
+    if t < 0:
+        raise MXFP8Error("mxfp8_gemm_tiles_per_chunk", EINVAL)
+    return t
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _rows_view(x: torch.Tensor, name: str, dtype):
+    _dev(x, name)
+    if x.dtype != dtype or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D {dtype} tensor with unit column stride")
+    return x
+
+
+def quantize(x: torch.Tensor, linear: bool = True, swizzled: bool = True, out=None):
+    """BF16 ``x [rows, k]`` (row stride may exceed k) -> ``(q [rows,k] u8, scales_linear, scales_swizzled)``.
+
+    ``out`` may pass preallocated ``(q, s_lin, s_swz)``; a scale layout not requested is None.
+    """
+    _rows_view(x, "x", torch.bfloat16)
+    rows, k = x.shape
+    if out is not None:
+        q, s_lin, s_swz = out
+    else:
+        q = torch.empty((rows, k), dtype=torch.uint8, device=x.device)
+        s_lin = torch.empty((rows, k // 32), dtype=torch.uint8, device=x.device) if linear else None
+        s_swz = torch.empty(scale_bytes(rows, k, SWIZZLED), dtype=torch.uint8, device=x.device) if swizzled else None
+    st = load_library().mxfp8_quantize(_ptr(x), rows, k, x.stride(0), _ptr(q), _ptr(s_lin), _ptr(s_swz), _stream(x))
+    if st != OK:
+        raise MXFP8Error("mxfp8_quantize", st)
+    return q, s_lin, s_swz
+
+
+def rmsnorm_quant(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, linear: bool = True,
+                  swizzled: bool = True, out=None):
+    """Gemma RMSNorm ``x / sqrt(mean(x^2) + eps) * (1 + w)`` quantised to MXFP8 in one pass.
+
+    Returns ``(q [rows, hidden] u8, scales_linear, scales_swizzled)``.
+    """
+    _rows_view(x, "x", torch.bfloat16)
+    _dev(w, "w")
+    rows, h = x.shape
+    if w.dtype != torch.bfloat16 or w.shape != (h,) or not w.is_contiguous():
+        raise ValueError("w must be a contiguous bfloat16 [hidden] tensor")
+    if out is not None:
+        q, s_lin, s_swz = out
+    else:
+        q = torch.empty((rows, h), dtype=torch.uint8, device=x.device)
+        s_lin = torch.empty((rows, h // 32), dtype=torch.uint8, device=x.device) if linear else None
+        s_swz = torch.empty(scale_bytes(rows, h, SWIZZLED), dtype=torch.uint8, device=x.device) if swizzled else None
+    st = load_library().rmsnorm_quant_mxfp8(_ptr(x), _ptr(w), rows, h, x.stride(0), float(eps), _ptr(q),
+                                            _ptr(s_lin), _ptr(s_swz), _stream(x))
+    if st != OK:
+        raise MXFP8Error("rmsnorm_quant_mxfp8", st)
+    return q, s_lin, s_swz
+
+
+def gemm(a: torch.Tensor, a_scales: torch.Tensor, a_layout: int, b: torch.Tensor, b_scales: torch.Tensor,
+         b_layout: int, out: torch.Tensor = None, num_chunks: int = 1, first_chunk: int = 0,
+         chunk_done: torch.Tensor = None) -> torch.Tensor:
+    """``C[m,n] = sum_k A[m,k] B[n,k]`` with UE8M0 block scales, BF16 out.
+
+    ``a`` E4M3 ``[m,k]`` u8 and ``b`` E4M3 ``[n,k]`` u8 (both contiguous); scales in the given
+    layouts. ``out`` (BF16 ``[m, >=n]``, unit column stride) is allocated when None. The output is
+    produced as ``num_chunks`` row chunks starting with ``first_chunk``; ``chunk_done`` (int32
+    ``[num_chunks]``, zeroed by the caller) counts finished tiles per chunk.
+    """
+    for t, nm in ((a, "a"), (b, "b"), (a_scales, "a_scales"), (b_scales, "b_scales")):
+        _dev(t, nm)
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous uint8 tensor")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
+        raise ValueError("a must be [m, k] and b [n, k]")
+    m, k = a.shape
+    n = b.shape[0]
+    if out is None:
+        ldc = (n + 3) // 4 * 4  # the kernels store 4 columns at a time: keep rows 8-byte aligned
+        out = torch.empty((m, ldc), dtype=torch.bfloat16, device=a.device)[:, :n]
+    _rows_view(out, "out", torch.bfloat16)
+    if out.shape[0] != m or out.shape[1] < n:
+        raise ValueError("out must be [m, >=n]")
+    if chunk_done is not None:
+        _dev(chunk_done, "chunk_done")
+        if chunk_done.dtype != torch.int32 or chunk_done.numel() < num_chunks or not chunk_done.is_contiguous():
+            raise ValueError("chunk_done must be a contiguous int32 tensor with num_chunks entries")
+    st = load_library().mxfp8_gemm_bf16out(_ptr(a), _ptr(a_scales), int(a_layout), _ptr(b), _ptr(b_scales),
+                                           int(b_layout), m, n, k, _ptr(out), out.stride(0), int(num_chunks),
+                                           int(first_chunk), _ptr(chunk_done), _stream(a))
+    if st != OK:
+        raise MXFP8Error("mxfp8_gemm_bf16out", st)
+    return out

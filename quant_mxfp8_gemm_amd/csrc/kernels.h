@@ -1,0 +1,31 @@
+// kernels.h - launchers of the MXFP8 kernels (internal to the library; the C ABI is include/mxfp8.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxfp8 {
+
+// Arguments are validated by the C-ABI layer before any launcher runs.
+hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* q,
+                           uint8_t* s_lin, uint8_t* s_swz, hipStream_t stream);
+
+hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* w, int64_t rows, int64_t hidden,
+                                int64_t ldx, float eps, uint8_t* q, uint8_t* s_lin, uint8_t* s_swz,
+                                hipStream_t stream);
+
+// Zero the pad bytes of a swizzled scale buffer for a [rows, k] operand (no-op without padding).
+hipError_t launch_swizzle_pad_zero(uint8_t* s_swz, int64_t rows, int64_t k, hipStream_t stream);
+
+struct GemmShape {
+  int bm, bn;  // output tile
+};
+
+// Tile shape the GEMM uses for this problem.
+GemmShape gemm_pick_shape(int64_t m, int64_t n, int num_chunks);
+
+hipError_t launch_gemm(const uint8_t* a, const uint8_t* as, int a_layout, const uint8_t* b,
+                       const uint8_t* bs, int b_layout, int64_t m, int64_t n, int64_t k, uint16_t* c,
+                       int64_t ldc, int num_chunks, int first_chunk, int* chunk_done, hipStream_t stream);
+
+}  // namespace mxfp8

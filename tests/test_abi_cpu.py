@@ -1,0 +1,123 @@
+"""The C ABI on the host (no GPU): the library loads, exports every function that
+include/*.h declares, and its argument checks return the documented status codes
+without touching the GPU."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import quant_mxfp8_gemm_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, EINVAL, EALIGN, EUNSUP = mx.OK, mx.EINVAL, mx.EALIGN, mx.EUNSUPPORTED
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s+\*?([a-z_][a-z0-9_]*)\s*\(", text, re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mx.LIB_PATH):
+        import quant_mxfp8_gemm_amd.build as b
+        b.build()
+    return mx.load_library()
+
+
+def test_header_declares_the_three_operations():
+    names = _declared_functions()
+    for f in ("mxfp8_quantize", "rmsnorm_quant_mxfp8", "mxfp8_gemm_bf16out", "mxfp8_scale_bytes",
+              "mxfp8_status_string"):
+        assert f in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in sorted(_declared_functions()):
+        assert hasattr(lib, name), name
+
+
+def test_scale_bytes(lib):
+    assert mx.scale_bytes(128, 128, mx.LINEAR) == 128 * 4
+    assert mx.scale_bytes(1024, 6144, mx.SWIZZLED) == 1024 * 192
+    assert mx.scale_bytes(200, 96, mx.SWIZZLED) == 256 * 4
+    assert mx.scale_bytes(1, 32, mx.SWIZZLED) == 512
+    assert lib.mxfp8_scale_bytes(10, 33, 0) == -1
+    assert lib.mxfp8_scale_bytes(10, 64, 7) == -1
+    assert lib.mxfp8_scale_bytes(-1, 64, 0) == -1
+
+
+def test_status_strings(lib):
+    for st in (OK, EINVAL, EALIGN, EUNSUP, mx.EHIP):
+        assert mx.status_string(st) and mx.status_string(st) != "unknown status"
+    assert mx.status_string(12345) == "unknown status"
+
+
+P = 1 << 20  # a fake 1 MiB-aligned address: the checks never dereference pointers
+
+
+def test_quantize_check(lib):
+    c = lib.mxfp8_quantize_check
+    assert c(P, 128, 2048, 2048, P, P, P) == OK
+    assert c(P, 128, 2048, 2048, P, None, P) == OK
+    assert c(P, 0, 2048, 2048, P, P, None) == OK
+    assert c(None, 0, 2048, 2048, None, None, None) == OK  # rows == 0: nothing is touched
+    assert c(P, 128, 2047, 2048, P, P, P) == EINVAL      # k % 32
+    assert c(P, 128, 2048, 2040, P, P, P) == EINVAL      # ldx < k
+    assert c(P, -1, 2048, 2048, P, P, P) == EINVAL
+    assert c(P, 128, 2048, 2048, P, None, None) == EINVAL
+    assert c(None, 128, 2048, 2048, P, P, P) == EINVAL
+    assert c(P + 8, 128, 2048, 2048, P, P, P) == EALIGN   # x not 16-byte aligned
+    assert c(P, 128, 2048, 2052, P, P, P) == EALIGN       # ldx % 8
+    assert c(P, 128, 2048, 2048, P + 4, P, P) == EALIGN   # q not 8-byte aligned
+
+
+def test_rmsnorm_check(lib):
+    c = lib.rmsnorm_quant_mxfp8_check
+    assert c(P, P, 1024, 6144, 6144, P, P, P) == OK
+    assert c(P, P, 1024, 6144, 6144, P, None, None) == EINVAL
+    assert c(P, None, 1024, 6144, 6144, P, P, P) == EINVAL
+    assert c(P, P, 1024, 6150, 6150, P, P, P) == EINVAL
+    assert c(P, P, 1024, 32768, 32768, P, P, P) == EUNSUP
+    assert c(P, P + 2, 1024, 6144, 6144, P, P, P) == EALIGN
+
+
+def test_gemm_check(lib):
+    c = lib.mxfp8_gemm_bf16out_check
+    good = dict(a=P, sa=P, la=0, b=P, sb=P, lb=1, m=4096, n=6144, k=3072, c=P, ldc=6144, nc=4, fc=0)
+
+    def call(**kw):
+        d = dict(good)
+        d.update(kw)
+        return c(d["a"], d["sa"], d["la"], d["b"], d["sb"], d["lb"], d["m"], d["n"], d["k"], d["c"], d["ldc"],
+                 d["nc"], d["fc"])
+
+    assert call() == OK
+    assert call(m=0) == EINVAL
+    assert call(k=3000) == EINVAL          # k % 32
+    assert call(k=3040) == EUNSUP          # k % 128
+    assert call(la=2) == EINVAL
+    assert call(ldc=6000) == EINVAL
+    assert call(nc=3) == EINVAL            # 4096 % 3
+    assert call(fc=4) == EINVAL
+    assert call(fc=-1) == EINVAL
+    assert call(nc=0) == EINVAL
+    assert call(sb=None) == EINVAL
+    assert call(a=P + 8) == EALIGN
+    assert call(sa=P + 2) == EALIGN
+    assert call(c=P + 4) == EALIGN
+    assert call(ldc=6146) == EALIGN
+    assert call(m=1 << 20, k=3072) == EUNSUP   # operand beyond 2 GiB
+
+
+def test_tiles_per_chunk(lib):
+    t = mx.gemm_tiles_per_chunk(32768, 6144, 4)
+    assert t > 0 and t * 4 * 256 * 256 >= 32768 * 6144
+    assert lib.mxfp8_gemm_tiles_per_chunk(10, 10, 3) == -1
