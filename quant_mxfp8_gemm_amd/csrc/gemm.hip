@@ -7,25 +7,29 @@
 // match one rank's reduce-scatter shard ("Overview", "Details").
 //
 // Design (CDNA4):
-//  * One workgroup = 4 waves (2 x 2) computes a BM x BN output tile; each wave owns a
-//    (BM/2) x (BN/2) sub-tile made of 32x32 MFMA blocks accumulated in fp32.
-//  * V_MFMA_SCALE_F32_32X32X64_F8F6F4 applies the UE8M0 block scales inside the instruction.
-//    Operand layout of that instruction (32 rows x 64 K per operand): lane l holds row l%32;
-//    with g = l/32, its bytes 0..15 are K 16g..16g+15 and bytes 16..31 are K 32+16g..32+16g+15.
-//    The scale of (row r, 32-block b) comes from lane r + 32b, byte selected by OPSEL.
-//    Result lane l, register v: column l%32, row 8(v/4) + 4(l/32) + v%4.
-//  * The B tile (output columns n) is fed as the instruction's first operand and the A tile as
-//    the second, so each lane ends up with runs of 4 consecutive n of one output row m and the
-//    epilogue stores 8 bytes per run.
-//  * K advances 128 bytes per stage. Stages are double-buffered in LDS and filled directly from
-//    global memory with 16-byte LDS-DMA loads (global_load_lds_dwordx4). A row of a stage is
-//    8 chunks of 16 bytes; chunk c of row r sits in slot c ^ ((r ^ (r >> 3)) & 7), so the 16
-//    consecutive rows one ds_read_b128 touches spread over all banks.
-//  * The 4 scale bytes of a row for one stage form one aligned dword in both scale layouts;
-//    each lane loads the dwords of its rows one stage ahead and keeps the two bytes it needs.
-//  * Tile order: chunk by chunk from first_chunk; inside a chunk every XCD (workgroups are
-//    dispatched round-robin over 8 XCDs) gets a contiguous run of tiles, grouped GM tile-rows
-//    tall so that concurrently running tiles share A and B panels in that XCD's L2.
+//  * Persistent grid: one 8-wave workgroup per CU walks the output tiles in dispatch order.
+//    Tile order: chunk by chunk from first_chunk; inside a chunk every XCD (workgroups are
+//    placed round-robin over the 8 XCDs) gets a contiguous run of tiles, grouped GM tile-rows
+//    tall, so the 32 tiles an XCD works on at once share A and B panels in its L2.
+//  * A 256 x 256 output tile is split over 8 waves as 4 x 2; each wave owns 64 x 128, i.e.
+//    2 x 4 blocks of V_MFMA_SCALE_F32_32X32X64_F8F6F4 accumulated in fp32. Two waves share
+//    each SIMD, so one issues MFMAs while the other waits on LDS.
+//  * The instruction applies the UE8M0 block scales itself. Operand layout (32 rows x 64 K):
+//    lane l holds row l%32; with g = l/32, its bytes 0..15 are K 16g..16g+15 and bytes 16..31
+//    are K 32+16g..32+16g+15. The scale of (row r, 32-block b) comes from lane r + 32b, byte
+//    selected by OPSEL. Result lane l, register v: column l%32, row 8(v/4) + 4(l/32) + v%4.
+//    B (output columns n) is fed as the first operand and A as the second, so each lane
+//    holds runs of 4 consecutive n of one output row m.
+//  * K advances 128 bytes per stage (one full 128-byte line per row). Two stages of A, B and
+//    their scale dwords live in LDS and are filled by LDS-DMA loads (global_load_lds, 16 bytes
+//    per lane for data, 4 for scales) straight from memory. A row of a stage is 8 chunks of
+//    16 bytes; chunk c of row r sits in slot c ^ ((r ^ (r >> 3)) & 7), so the rows read by one
+//    ds_read_b128 spread over all banks. The 4 scale bytes of a row for one stage are one
+//    aligned dword in both scale layouts.
+//  * Epilogue: the tile is converted to BF16 into LDS (both stage buffers, rows padded by
+//    16 bytes) and written back with 16-byte streaming stores, every row a run of full lines.
+#include <atomic>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -38,15 +42,22 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BK = 128;  // K bytes per stage
-constexpr int NT = 256;  // 4 waves
 constexpr int GM = 4;    // tile-rows per group
 
-template <int BM, int BN>
+template <int BM, int BN, int WMW, int WNW>
 struct Tile {
-  static constexpr int WM = BM / 2, WN = BN / 2;    // wave sub-tile
-  static constexpr int TM = WM / 32, TN = WN / 32;  // MFMA blocks per wave
-  static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
-  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int NW = WMW * WNW, NT = NW * 64;
+  static constexpr int WTM = BM / WMW, WTN = BN / WNW;  // wave sub-tile
+  static constexpr int TM = WTM / 32, TN = WTN / 32;    // MFMA blocks per wave
+  static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, SC_BYTES = (BM + BN) * 4;
+  static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
+  static constexpr int DA = A_BYTES / 1024 / NW;  // 1 KiB data loads per wave per stage
+  static constexpr int DB = B_BYTES / 1024 / NW;
+  static constexpr int DS = (BM + BN) / 64 / NW;  // 256-byte scale loads per wave per stage
+  static constexpr int C_STRIDE = BN * 2 + 16;    // bytes per staged output row
+  static_assert(DA * NW * 1024 == A_BYTES && DB * NW * 1024 == B_BYTES && DS * NW * 64 == BM + BN, "split");
+  static_assert(BM * C_STRIDE <= 2 * STAGE, "output staging must fit in the stage buffers");
+  static_assert((BM * BN / 8) % NT == 0, "epilogue rows");
 };
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
@@ -54,219 +65,222 @@ __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 // Byte offset, inside one stage's A or B region, of logical 16-byte chunk c of row r.
 __device__ __forceinline__ int lds_off(int r, int c) { return (r * 8 + (c ^ swz(r))) * 16; }
 
-// Scaled MFMA with compile-time byte selectors.
 template <int SEL>
 __device__ __forceinline__ v16f mfma(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SEL, sa, SEL, sb);
 }
 
-// Offset of the 4-byte scale group (row r, stage kt) in the given layout; nblk4 = K/128.
+// Offset of the 4-byte scale group (row r, 128-K step 0) in the given layout; nblk4 = K/128.
 template <int LAYOUT>
-__device__ __forceinline__ uint32_t scale_dword_off(uint32_t r, uint32_t kt, uint32_t nblk4) {
-  if (LAYOUT == 0) return (r * nblk4 + kt) * 4;
-  return ((r >> 7) * nblk4 + kt) * 512 + (r & 31) * 16 + ((r >> 5) & 3) * 4;
+__device__ __forceinline__ uint32_t scale_base(uint32_t r, uint32_t nblk4) {
+  if (LAYOUT == 0) return r * nblk4 * 4;
+  return (r >> 7) * nblk4 * 512 + (r & 31) * 16 + ((r >> 5) & 3) * 4;
 }
+// Distance between consecutive 128-K steps of one row's scale dwords.
+template <int LAYOUT>
+constexpr uint32_t scale_step() { return LAYOUT == 0 ? 4u : 512u; }
 
-// Issue the LDS-DMA loads of one R-row x 128-byte operand tile: R/8 instructions of 1 KiB,
-// R/32 per wave. src_off[i] is the lane's byte offset (row * K + chunk * 16) for instruction i.
-template <int R>
-__device__ __forceinline__ void issue_tile(const uint8_t* __restrict__ base, const uint32_t* src_off,
-                                           uint32_t k0, uint8_t* lds_region, int wave) {
-#pragma unroll
-  for (int i = 0; i < R / 32; ++i) {
-    const int inst = wave * (R / 32) + i;
-    __builtin_amdgcn_global_load_lds((const void*)(base + src_off[i] + k0),
-                                     (lds_void*)(lds_region + inst * 1024), 16, 0, 0);
-  }
-}
-
-template <int BM, int BN, int A_LAYOUT, int B_LAYOUT>
-__global__ __launch_bounds__(NT, 1) void gemm_kernel(const uint8_t* __restrict__ A,
-                                                     const uint8_t* __restrict__ As,
-                                                     const uint8_t* __restrict__ B,
-                                                     const uint8_t* __restrict__ Bs,
-                                                     uint16_t* __restrict__ C, int M, int N, int K,
-                                                     int ldc, int num_chunks, int first_chunk,
-                                                     int* __restrict__ chunk_done) {
-  using T = Tile<BM, BN>;
+template <int BM, int BN, int WMW, int WNW, int A_LAYOUT, int B_LAYOUT>
+__global__ __launch_bounds__(WMW * WNW * 64, 1) void gemm_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, uint16_t* __restrict__ C, int M, int N, int K, int ldc, int num_chunks,
+    int first_chunk, int* __restrict__ chunk_done, int wide_store) {
+  using T = Tile<BM, BN, WMW, WNW>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WNW, wn = wave % WNW;
   const int l32 = lane & 31, g = lane >> 5;
 
-  // ---- tile coordinates: chunk-major, XCD-contiguous, grouped
   const int chunk_rows = M / num_chunks;
   const int tiles_n = (N + BN - 1) / BN;
   const int tiles_mc = (chunk_rows + BM - 1) / BM;
   const int tpc = tiles_mc * tiles_n;
-  const int bid = blockIdx.x;
-  const int ci = bid / tpc;
-  const int j = bid - ci * tpc;
-  const int chunk = (first_chunk + ci) % num_chunks;
-  const int lj = (tpc % 8 == 0) ? (j % 8) * (tpc / 8) + j / 8 : j;
-  const int group = lj / (GM * tiles_n);
-  const int first_tm = group * GM;
-  const int gsz = min(tiles_mc - first_tm, GM);
-  const int tm_idx = first_tm + (lj % (GM * tiles_n)) % gsz;
-  const int tn_idx = (lj % (GM * tiles_n)) / gsz;
-  const int chunk_m0 = chunk * chunk_rows;
-  const int m0 = chunk_m0 + tm_idx * BM;
-  const int m_end = min(m0 + BM, chunk_m0 + chunk_rows);
-  const int n0 = tn_idx * BN;
-
-  // ---- per-lane LDS-DMA source offsets (rows clamped into the operand; surplus rows unused)
-  uint32_t a_off[BM / 32], b_off[BN / 32];
-#pragma unroll
-  for (int i = 0; i < BM / 32; ++i) {
-    const int s = (wave * (BM / 32) + i) * 64 + lane;
-    const int r = s >> 3;
-    const int c = (s & 7) ^ swz(r);
-    a_off[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + c * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < BN / 32; ++i) {
-    const int s = (wave * (BN / 32) + i) * 64 + lane;
-    const int r = s >> 3;
-    const int c = (s & 7) ^ swz(r);
-    b_off[i] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + c * 16;
-  }
-
-  // ---- per-lane scale rows
-  const uint32_t nblk4 = (uint32_t)K / 128;
-  uint32_t a_srow[T::TM], b_srow[T::TN];
-#pragma unroll
-  for (int t = 0; t < T::TM; ++t) a_srow[t] = (uint32_t)min(m0 + wm * T::WM + t * 32 + l32, M - 1);
-#pragma unroll
-  for (int t = 0; t < T::TN; ++t) b_srow[t] = (uint32_t)min(n0 + wn * T::WN + t * 32 + l32, N - 1);
-
-  v16f acc[T::TN][T::TM];
-#pragma unroll
-  for (int x = 0; x < T::TN; ++x)
-#pragma unroll
-    for (int y = 0; y < T::TM; ++y)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.f;
-
+  const int total = tpc * num_chunks;
   const int KT = K / BK;
-  uint32_t asc[T::TM], bsc[T::TN];
+  const uint32_t nblk4 = (uint32_t)K / 128;
 
-  // prologue: stage 0
-  issue_tile<BM>(A, a_off, 0, smem, wave);
-  issue_tile<BN>(B, b_off, 0, smem + T::A_BYTES, wave);
-#pragma unroll
-  for (int t = 0; t < T::TM; ++t) asc[t] = *(const uint32_t*)(As + scale_dword_off<A_LAYOUT>(a_srow[t], 0, nblk4));
-#pragma unroll
-  for (int t = 0; t < T::TN; ++t) bsc[t] = *(const uint32_t*)(Bs + scale_dword_off<B_LAYOUT>(b_srow[t], 0, nblk4));
+  for (int bid = blockIdx.x; bid < total; bid += gridDim.x) {
+    // ---- tile coordinates
+    const int ci = bid / tpc;
+    const int j = bid - ci * tpc;
+    const int chunk = (first_chunk + ci) % num_chunks;
+    const int lj = (tpc % 8 == 0) ? (j % 8) * (tpc / 8) + j / 8 : j;
+    const int group = lj / (GM * tiles_n);
+    const int first_tm = group * GM;
+    const int gsz = min(tiles_mc - first_tm, GM);
+    const int tm_idx = first_tm + (lj % (GM * tiles_n)) % gsz;
+    const int tn_idx = (lj % (GM * tiles_n)) / gsz;
+    const int chunk_m0 = chunk * chunk_rows;
+    const int m0 = chunk_m0 + tm_idx * BM;
+    const int m_end = min(m0 + BM, chunk_m0 + chunk_rows);
+    const int n0 = tn_idx * BN;
 
-  for (int kt = 0; kt < KT; ++kt) {
-    uint8_t* cur = smem + (kt & 1) * T::STAGE;
-    uint8_t* nxt = smem + ((kt + 1) & 1) * T::STAGE;
-    // this stage's loads have landed in LDS for every wave; the other buffer is free
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    // this lane's scale bytes for the stage: byte 0 -> block g (first MFMA), byte 2 -> block 2+g
-    uint32_t as_sel[T::TM], bs_sel[T::TN];
+    // ---- per-lane LDS-DMA sources (rows clamped into the operand; surplus rows are not stored)
+    uint32_t a_off[T::DA], b_off[T::DB], s_off[T::DS];
+    const uint8_t* s_src[T::DS];
+    uint32_t s_step[T::DS];
 #pragma unroll
-    for (int t = 0; t < T::TM; ++t) as_sel[t] = (asc[t] >> (8 * g)) & 0x00FF00FFu;
+    for (int i = 0; i < T::DA; ++i) {
+      const int s = (wave * T::DA + i) * 64 + lane;
+      const int r = s >> 3;
+      a_off[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + (((s & 7) ^ swz(r)) * 16);
+    }
 #pragma unroll
-    for (int t = 0; t < T::TN; ++t) bs_sel[t] = (bsc[t] >> (8 * g)) & 0x00FF00FFu;
-
-    if (kt + 1 < KT) {
-      const uint32_t k0 = (uint32_t)(kt + 1) * BK;
-      issue_tile<BM>(A, a_off, k0, nxt, wave);
-      issue_tile<BN>(B, b_off, k0, nxt + T::A_BYTES, wave);
+    for (int i = 0; i < T::DB; ++i) {
+      const int s = (wave * T::DB + i) * 64 + lane;
+      const int r = s >> 3;
+      b_off[i] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + (((s & 7) ^ swz(r)) * 16);
+    }
 #pragma unroll
-      for (int t = 0; t < T::TM; ++t)
-        asc[t] = *(const uint32_t*)(As + scale_dword_off<A_LAYOUT>(a_srow[t], kt + 1, nblk4));
-#pragma unroll
-      for (int t = 0; t < T::TN; ++t)
-        bsc[t] = *(const uint32_t*)(Bs + scale_dword_off<B_LAYOUT>(b_srow[t], kt + 1, nblk4));
+    for (int i = 0; i < T::DS; ++i) {
+      const int row = (wave * T::DS + i) * 64 + lane;  // A rows, then B rows
+      if (row < BM) {
+        s_src[i] = As;
+        s_off[i] = scale_base<A_LAYOUT>((uint32_t)min(m0 + row, M - 1), nblk4);
+        s_step[i] = scale_step<A_LAYOUT>();
+      } else {
+        s_src[i] = Bs;
+        s_off[i] = scale_base<B_LAYOUT>((uint32_t)min(n0 + row - BM, N - 1), nblk4);
+        s_step[i] = scale_step<B_LAYOUT>();
+      }
     }
 
-    const uint8_t* a_lds = cur;
-    const uint8_t* b_lds = cur + T::A_BYTES;
+    auto issue = [&](int kt) {
+      uint8_t* st = smem + (kt & 1) * T::STAGE;
+      const uint32_t k0 = (uint32_t)kt * BK;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      v8i af[T::TM], bf[T::TN];
+      for (int i = 0; i < T::DA; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(A + a_off[i] + k0),
+                                         (lds_void*)(st + (wave * T::DA + i) * 1024), 16, 0, 0);
 #pragma unroll
-      for (int t = 0; t < T::TM; ++t) {
-        const int r = wm * T::WM + t * 32 + l32;
-        const v4i lo = *(const v4i*)(a_lds + lds_off(r, 4 * ks + g));
-        const v4i hi = *(const v4i*)(a_lds + lds_off(r, 4 * ks + 2 + g));
-        af[t] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
+      for (int i = 0; i < T::DB; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(B + b_off[i] + k0),
+                                         (lds_void*)(st + T::A_BYTES + (wave * T::DB + i) * 1024), 16, 0, 0);
 #pragma unroll
-      for (int t = 0; t < T::TN; ++t) {
-        const int r = wn * T::WN + t * 32 + l32;
-        const v4i lo = *(const v4i*)(b_lds + lds_off(r, 4 * ks + g));
-        const v4i hi = *(const v4i*)(b_lds + lds_off(r, 4 * ks + 2 + g));
-        bf[t] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      }
+      for (int i = 0; i < T::DS; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(s_src[i] + s_off[i] + (uint32_t)kt * s_step[i]),
+                                         (lds_void*)(st + T::A_BYTES + T::B_BYTES + (wave * T::DS + i) * 256),
+                                         4, 0, 0);
+    };
+
+    v16f acc[T::TN][T::TM];
 #pragma unroll
-      for (int x = 0; x < T::TN; ++x)
+    for (int x = 0; x < T::TN; ++x)
 #pragma unroll
-        for (int y = 0; y < T::TM; ++y) {
-          if (ks == 0)
-            acc[x][y] = mfma<0>(bf[x], af[y], acc[x][y], (int)bs_sel[x], (int)as_sel[y]);
-          else
-            acc[x][y] = mfma<2>(bf[x], af[y], acc[x][y], (int)bs_sel[x], (int)as_sel[y]);
+      for (int y = 0; y < T::TM; ++y)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.f;
+
+    __syncthreads();  // the previous tile's epilogue is done with LDS
+    issue(0);
+    for (int kt = 0; kt < KT; ++kt) {
+      // this stage's loads have landed in LDS for every wave; the other buffer is free
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (kt + 1 < KT) issue(kt + 1);
+
+      const uint8_t* st = smem + (kt & 1) * T::STAGE;
+      const uint8_t* a_lds = st;
+      const uint8_t* b_lds = st + T::A_BYTES;
+      const uint32_t* sc = (const uint32_t*)(st + T::A_BYTES + T::B_BYTES);
+      // this lane's scale bytes: byte 0 -> block g (first 64 K), byte 2 -> block 2+g (second 64 K)
+      uint32_t as_sel[T::TM], bs_sel[T::TN];
+#pragma unroll
+      for (int t = 0; t < T::TM; ++t) as_sel[t] = (sc[wm * T::WTM + t * 32 + l32] >> (8 * g)) & 0x00FF00FFu;
+#pragma unroll
+      for (int t = 0; t < T::TN; ++t) bs_sel[t] = (sc[BM + wn * T::WTN + t * 32 + l32] >> (8 * g)) & 0x00FF00FFu;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        v8i af[T::TM], bf[T::TN];
+#pragma unroll
+        for (int t = 0; t < T::TM; ++t) {
+          const int r = wm * T::WTM + t * 32 + l32;
+          const v4i lo = *(const v4i*)(a_lds + lds_off(r, 4 * ks + g));
+          const v4i hi = *(const v4i*)(a_lds + lds_off(r, 4 * ks + 2 + g));
+          af[t] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
+#pragma unroll
+        for (int t = 0; t < T::TN; ++t) {
+          const int r = wn * T::WTN + t * 32 + l32;
+          const v4i lo = *(const v4i*)(b_lds + lds_off(r, 4 * ks + g));
+          const v4i hi = *(const v4i*)(b_lds + lds_off(r, 4 * ks + 2 + g));
+          bf[t] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int x = 0; x < T::TN; ++x)
+#pragma unroll
+          for (int y = 0; y < T::TM; ++y) {
+            if (ks == 0)
+              acc[x][y] = mfma<0>(bf[x], af[y], acc[x][y], (int)bs_sel[x], (int)as_sel[y]);
+            else
+              acc[x][y] = mfma<2>(bf[x], af[y], acc[x][y], (int)bs_sel[x], (int)as_sel[y]);
+          }
+      }
     }
-  }
 
-  // ---- epilogue: lane holds C[m = row0 + l32][n = col0 + 8*(v/4) + 4*g + v%4]
+    // ---- epilogue: BF16 tile staged in LDS, then full-line 16-byte stores
+    __syncthreads();  // every wave is done reading the last stage
 #pragma unroll
-  for (int x = 0; x < T::TN; ++x) {
+    for (int x = 0; x < T::TN; ++x) {
 #pragma unroll
-    for (int y = 0; y < T::TM; ++y) {
-      const int m = m0 + wm * T::WM + y * 32 + l32;
-      if (m >= m_end) continue;
-      uint16_t* crow = C + (int64_t)m * ldc;
+      for (int y = 0; y < T::TM; ++y) {
+        const int r = wm * T::WTM + y * 32 + l32;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * T::WN + x * 32 + 8 * q + 4 * g;
-        const uint32_t b0 = f32_to_bf16_rne(acc[x][y][4 * q + 0]);
-        const uint32_t b1 = f32_to_bf16_rne(acc[x][y][4 * q + 1]);
-        const uint32_t b2 = f32_to_bf16_rne(acc[x][y][4 * q + 2]);
-        const uint32_t b3 = f32_to_bf16_rne(acc[x][y][4 * q + 3]);
-        if (n + 3 < N) {
-          *(uint2*)(crow + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+        for (int q = 0; q < 4; ++q) {
+          const int c = wn * T::WTN + x * 32 + 8 * q + 4 * g;
+          const uint32_t lo = f32_to_bf16_rne(acc[x][y][4 * q + 0]) | (f32_to_bf16_rne(acc[x][y][4 * q + 1]) << 16);
+          const uint32_t hi = f32_to_bf16_rne(acc[x][y][4 * q + 2]) | (f32_to_bf16_rne(acc[x][y][4 * q + 3]) << 16);
+          *(uint2*)(smem + r * T::C_STRIDE + c * 2) = make_uint2(lo, hi);
+        }
+      }
+    }
+    __syncthreads();
+    constexpr int SEGS = BN / 8;  // 16-byte segments per row
+#pragma unroll 4
+    for (int p = tid; p < BM * SEGS; p += T::NT) {
+      const int r = p / SEGS;
+      const int c8 = (p % SEGS) * 8;
+      const int m = m0 + r;
+      const int n = n0 + c8;
+      if (m >= m_end || n >= N) continue;
+      const uint4 v = *(const uint4*)(smem + r * T::C_STRIDE + c8 * 2);
+      uint16_t* dst = C + (int64_t)m * ldc + n;
+      if (n + 8 <= N) {
+        if (wide_store) {
+          __builtin_nontemporal_store(*(const u32x4*)&v, (u32x4*)dst);
         } else {
-          if (n + 0 < N) crow[n + 0] = (uint16_t)b0;
-          if (n + 1 < N) crow[n + 1] = (uint16_t)b1;
-          if (n + 2 < N) crow[n + 2] = (uint16_t)b2;
+          *(uint2*)dst = make_uint2(v.x, v.y);
+          *(uint2*)(dst + 4) = make_uint2(v.z, v.w);
         }
+      } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        for (int e = 0; e < N - n; ++e) dst[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
       }
     }
-  }
 
-  if (chunk_done != nullptr) {
-    __threadfence();  // this thread's C stores are visible device-wide
-    __syncthreads();
-    if (tid == 0) atomicAdd(chunk_done + chunk, 1);
+    if (chunk_done != nullptr) {
+      __threadfence();  // this thread's C stores are visible device-wide
+      __syncthreads();
+      if (tid == 0) atomicAdd(chunk_done + chunk, 1);
+    }
   }
 }
 
-template <int BM, int BN>
-hipError_t launch_shape(const uint8_t* a, const uint8_t* as, int a_layout, const uint8_t* b, const uint8_t* bs,
-                        int b_layout, int m, int n, int k, uint16_t* c, int ldc, int num_chunks, int first_chunk,
-                        int* chunk_done, hipStream_t stream) {
-  const int chunk_rows = m / num_chunks;
-  const int64_t tiles = (int64_t)num_chunks * ((chunk_rows + BM - 1) / BM) * ((n + BN - 1) / BN);
-  const dim3 grid((unsigned)tiles), block(NT);
-  if (a_layout == 0 && b_layout == 0)
-    gemm_kernel<BM, BN, 0, 0><<<grid, block, 0, stream>>>(a, as, b, bs, c, m, n, k, ldc, num_chunks, first_chunk, chunk_done);
-  else if (a_layout == 0 && b_layout == 1)
-    gemm_kernel<BM, BN, 0, 1><<<grid, block, 0, stream>>>(a, as, b, bs, c, m, n, k, ldc, num_chunks, first_chunk, chunk_done);
-  else if (a_layout == 1 && b_layout == 0)
-    gemm_kernel<BM, BN, 1, 0><<<grid, block, 0, stream>>>(a, as, b, bs, c, m, n, k, ldc, num_chunks, first_chunk, chunk_done);
-  else
-    gemm_kernel<BM, BN, 1, 1><<<grid, block, 0, stream>>>(a, as, b, bs, c, m, n, k, ldc, num_chunks, first_chunk, chunk_done);
-  return hipGetLastError();
+constexpr int TILE_M = 256, TILE_N = 256, WAVES_M = 4, WAVES_N = 2;
+
+int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cached[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 }  // namespace
@@ -275,16 +289,32 @@ GemmShape gemm_pick_shape(int64_t m, int64_t n, int num_chunks) {
   (void)m;
   (void)n;
   (void)num_chunks;
-  return GemmShape{256, 256};
+  return GemmShape{TILE_M, TILE_N};
 }
 
 hipError_t launch_gemm(const uint8_t* a, const uint8_t* as, int a_layout, const uint8_t* b,
                        const uint8_t* bs, int b_layout, int64_t m, int64_t n, int64_t k, uint16_t* c,
                        int64_t ldc, int num_chunks, int first_chunk, int* chunk_done, hipStream_t stream) {
-  const GemmShape s = gemm_pick_shape(m, n, num_chunks);
-  (void)s;
-  return launch_shape<256, 256>(a, as, a_layout, b, bs, b_layout, (int)m, (int)n, (int)k, c, (int)ldc, num_chunks,
-                                first_chunk, chunk_done, stream);
+  const int64_t chunk_rows = m / num_chunks;
+  const int64_t tiles = (int64_t)num_chunks * ((chunk_rows + TILE_M - 1) / TILE_M) * ((n + TILE_N - 1) / TILE_N);
+  const int64_t grid = tiles < device_cu_count() ? tiles : device_cu_count();
+  const int wide = ((uintptr_t)c % 16 == 0 && ldc % 8 == 0) ? 1 : 0;
+  const dim3 g((unsigned)grid), blk(WAVES_M * WAVES_N * 64);
+  const int M = (int)m, N = (int)n, K = (int)k, L = (int)ldc;
+#define MXFP8_GEMM_LAUNCH(AL, BL)                                                                   \
+  gemm_kernel<TILE_M, TILE_N, WAVES_M, WAVES_N, AL, BL><<<g, blk, 0, stream>>>(a, as, b, bs, c, M, N, K, L, \
+                                                                               num_chunks, first_chunk, \
+                                                                               chunk_done, wide)
+  if (a_layout == 0 && b_layout == 0)
+    MXFP8_GEMM_LAUNCH(0, 0);
+  else if (a_layout == 0 && b_layout == 1)
+    MXFP8_GEMM_LAUNCH(0, 1);
+  else if (a_layout == 1 && b_layout == 0)
+    MXFP8_GEMM_LAUNCH(1, 0);
+  else
+    MXFP8_GEMM_LAUNCH(1, 1);
+#undef MXFP8_GEMM_LAUNCH
+  return hipGetLastError();
 }
 
 }  // namespace mxfp8
