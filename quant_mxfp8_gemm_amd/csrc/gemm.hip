@@ -62,6 +62,11 @@ struct Tile {
 
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
+// Workgroup barrier without a memory fence. LDS-DMA completions are waited for explicitly
+// (vmcnt) before it, and each wave drains its own LDS accesses (lgkmcnt) so no buffer is
+// refilled or reread under a pending access; the epilogue's global stores need not drain.
+__device__ __forceinline__ void block_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Byte offset, inside one stage's A or B region, of logical 16-byte chunk c of row r.
 __device__ __forceinline__ int lds_off(int r, int c) { return (r * 8 + (c ^ swz(r))) * 16; }
 
@@ -174,12 +179,12 @@ __global__ __launch_bounds__(WMW * WNW * 64, 1) void gemm_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.f;
 
-    __syncthreads();  // the previous tile's epilogue is done with LDS
+    block_barrier();  // the previous tile's epilogue is done with LDS
     issue(0);
     for (int kt = 0; kt < KT; ++kt) {
       // this stage's loads have landed in LDS for every wave; the other buffer is free
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      block_barrier();
       if (kt + 1 < KT) issue(kt + 1);
 
       const uint8_t* st = smem + (kt & 1) * T::STAGE;
@@ -222,7 +227,7 @@ __global__ __launch_bounds__(WMW * WNW * 64, 1) void gemm_kernel(
     }
 
     // ---- epilogue: BF16 tile staged in LDS, then full-line 16-byte stores
-    __syncthreads();  // every wave is done reading the last stage
+    block_barrier();  // every wave is done reading the last stage
 #pragma unroll
     for (int x = 0; x < T::TN; ++x) {
 #pragma unroll
@@ -237,7 +242,7 @@ __global__ __launch_bounds__(WMW * WNW * 64, 1) void gemm_kernel(
         }
       }
     }
-    __syncthreads();
+    block_barrier();
     constexpr int SEGS = BN / 8;  // 16-byte segments per row
 #pragma unroll 4
     for (int p = tid; p < BM * SEGS; p += T::NT) {
