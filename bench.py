@@ -217,12 +217,15 @@ def main():
 
 
 def sweep(args, mx, synth, torch, dev):
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # evict the 256 MB MALL and the L2 with a 512 MiB read (a read leaves no dirty lines behind
+    # whose write-back would be charged to the next timed kernel)
+    flush = torch.ones(64 << 20, dtype=torch.int64, device=dev)
+    flush_out = torch.empty((), dtype=torch.int64, device=dev)
 
     def timed(fn, iters):
         ts = []
         for _ in range(iters):
-            flush.fill_(1)
+            torch.sum(flush, dim=0, out=flush_out)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             fn()

@@ -8,7 +8,8 @@
 // on the BF16 magnitude bits as integers (order-preserving for non-negative floats), the UE8M0
 // exponent comes straight from those bits, and the scaled values (exact power-of-two products)
 // go through the hardware fp32 -> E4M3 conversion, which rounds to nearest even.
-// Each lane keeps QU pieces in flight before converting any of them.
+// Each lane keeps QU pieces in flight before converting any of them. The codes are written
+// with streaming (non-temporal) stores: they are consumed by a later kernel, not re-read here.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -36,7 +37,7 @@ __global__ __launch_bounds__(QT) void quantize_kernel(const uint16_t* __restrict
     if (p < total) {
       const Idx r = p / cpr;
       const Idx c8 = p - r * cpr;
-      v[u] = load16_stream(x + r * ldx + c8 * 8);
+      v[u] = *(const uint4*)(x + r * ldx + c8 * 8);
     } else {
       v[u] = make_uint4(0u, 0u, 0u, 0u);
     }
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(QT) void quantize_kernel(const uint16_t* __restrict
     if (p < total) {
       const Idx r = p / cpr;
       const Idx c8 = p - r * cpr;
-      *(uint2*)(q + r * k + c8 * 8) = make_uint2(lo, hi);
+      __builtin_nontemporal_store(((uint64_t)hi << 32) | lo, (uint64_t*)(q + r * k + c8 * 8));
       if ((threadIdx.x & 3) == 0) {
         const Idx b = c8 >> 2;
         if (LIN) s_lin[r * nblk + b] = (uint8_t)s;

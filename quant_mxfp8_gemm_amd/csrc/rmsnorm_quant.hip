@@ -38,13 +38,18 @@ __global__ __launch_bounds__(RT) void rmsnorm_quant_kernel(const uint16_t* __res
   const int col_tiles = (nblk + 3) >> 2;
   const uint16_t* xr = x + row * ldx;
 
-  uint4 v[CPT];
+  uint4 v[CPT], wv[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {  // the weight row is loaded with x, not after the reduction
+    const int c8 = u * RT + (int)threadIdx.x;
+    wv[u] = c8 < cpr ? *(const uint4*)(w + c8 * 8) : make_uint4(0u, 0u, 0u, 0u);
+  }
   double ss = 0.0;
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
     const int c8 = u * RT + (int)threadIdx.x;
     if (c8 < cpr) {
-      v[u] = load16_stream(xr + c8 * 8);
+      v[u] = *(const uint4*)(xr + c8 * 8);
       const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -72,9 +77,8 @@ __global__ __launch_bounds__(RT) void rmsnorm_quant_kernel(const uint16_t* __res
     float y[8];
     uint32_t m = 0;
     if (live) {
-      const uint4 wv = *(const uint4*)(w + c8 * 8);
       const uint32_t xd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-      const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+      const uint32_t wd[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         y[2 * j] = (float)((double)bf16_lo(xd[j]) * rstd * (1.0 + (double)bf16_lo(wd[j])));
@@ -93,7 +97,7 @@ __global__ __launch_bounds__(RT) void rmsnorm_quant_kernel(const uint16_t* __res
     if (live) {
       const uint32_t lo = cvt_e4m3x4(y[0] * f, y[1] * f, y[2] * f, y[3] * f);
       const uint32_t hi = cvt_e4m3x4(y[4] * f, y[5] * f, y[6] * f, y[7] * f);
-      *(uint2*)(q + row * hidden + c8 * 8) = make_uint2(lo, hi);
+      __builtin_nontemporal_store(((uint64_t)hi << 32) | lo, (uint64_t*)(q + row * hidden + c8 * 8));
       if ((threadIdx.x & 3) == 0) {
         const int b = c8 >> 2;
         if (LIN) s_lin[row * nblk + b] = (uint8_t)s;
