@@ -11,22 +11,24 @@
 //    Tile order: chunk by chunk from first_chunk; inside a chunk every XCD (workgroups are
 //    placed round-robin over the 8 XCDs) gets a contiguous run of tiles, grouped GM tile-rows
 //    tall, so the 32 tiles an XCD works on at once share A and B panels in its L2.
-//  * A 256 x 256 output tile is split over 8 waves as 4 x 2; each wave owns 64 x 128, i.e.
-//    2 x 4 blocks of V_MFMA_SCALE_F32_32X32X64_F8F6F4 accumulated in fp32. Two waves share
-//    each SIMD, so one issues MFMAs while the other waits on LDS.
+//  * Large problems use a 256 x 256 output tile split over 8 waves as 4 x 2; each wave owns
+//    64 x 128, i.e. 2 x 4 blocks of V_MFMA_SCALE_F32_32X32X64_F8F6F4 accumulated in fp32.
+//    Two waves share each SIMD, so one issues MFMAs while the other waits on LDS. Problems
+//    with too few such tiles to fill the chip (few rows per chunk) use 128 x 128, 64 x 128
+//    or 32 x 128 tiles with four LDS stages, so three stages of loads are in flight.
 //  * The instruction applies the UE8M0 block scales itself. Operand layout (32 rows x 64 K):
 //    lane l holds row l%32; with g = l/32, its bytes 0..15 are K 16g..16g+15 and bytes 16..31
 //    are K 32+16g..32+16g+15. The scale of (row r, 32-block b) comes from lane r + 32b, byte
 //    selected by OPSEL. Result lane l, register v: column l%32, row 8(v/4) + 4(l/32) + v%4.
 //    B (output columns n) is fed as the first operand and A as the second, so each lane
 //    holds runs of 4 consecutive n of one output row m.
-//  * K advances 128 bytes per stage (one full 128-byte line per row). Two stages of A, B and
+//  * K advances 128 bytes per stage (one full 128-byte line per row). The stages of A, B and
 //    their scale dwords live in LDS and are filled by LDS-DMA loads (global_load_lds, 16 bytes
 //    per lane for data, 4 for scales) straight from memory. A row of a stage is 8 chunks of
 //    16 bytes; chunk c of row r sits in slot c ^ ((r ^ (r >> 3)) & 7), so the rows read by one
 //    ds_read_b128 spread over all banks. The 4 scale bytes of a row for one stage are one
 //    aligned dword in both scale layouts.
-//  * Epilogue: the tile is converted to BF16 into LDS (both stage buffers, rows padded by
+//  * Epilogue: the tile is converted to BF16 into LDS (over the stage buffers, rows padded by
 //    16 bytes) and written back with 16-byte streaming stores, every row a run of full lines.
 #include <atomic>
 
@@ -44,8 +46,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int BK = 128;  // K bytes per stage
 constexpr int GM = 4;    // tile-rows per group
 
-template <int BM, int BN, int WMW, int WNW>
+template <int BM_, int BN_, int WMW, int WNW, int NS_>
 struct Tile {
+  static constexpr int BM = BM_, BN = BN_, NS = NS_;
   static constexpr int NW = WMW * WNW, NT = NW * 64;
   static constexpr int WTM = BM / WMW, WTN = BN / WNW;  // wave sub-tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;    // MFMA blocks per wave
@@ -53,10 +56,15 @@ struct Tile {
   static constexpr int STAGE = A_BYTES + B_BYTES + SC_BYTES;
   static constexpr int DA = A_BYTES / 1024 / NW;  // 1 KiB data loads per wave per stage
   static constexpr int DB = B_BYTES / 1024 / NW;
-  static constexpr int DS = (BM + BN) / 64 / NW;  // 256-byte scale loads per wave per stage
+  static constexpr int SROWS = (BM + BN) / NW;    // scale rows (one dword each) per wave per stage
+  static constexpr int DS = (SROWS + 63) / 64;    // scale loads per wave per stage
+  static constexpr int LOADS = DA + DB + DS;      // LDS-DMA instructions per wave per stage
   static constexpr int C_STRIDE = BN * 2 + 16;    // bytes per staged output row
-  static_assert(DA * NW * 1024 == A_BYTES && DB * NW * 1024 == B_BYTES && DS * NW * 64 == BM + BN, "split");
-  static_assert(BM * C_STRIDE <= 2 * STAGE, "output staging must fit in the stage buffers");
+  static constexpr int LDS_BYTES = NS * STAGE > BM * C_STRIDE ? NS * STAGE : BM * C_STRIDE;
+  static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
+  static_assert(DA * NW * 1024 == A_BYTES && DB * NW * 1024 == B_BYTES, "data split");
+  static_assert(SROWS * NW == BM + BN && (SROWS % 64 == 0 || SROWS < 64), "scale split");
+  static_assert(NS >= 2 && LDS_BYTES <= 160 * 1024, "stages");
   static_assert((BM * BN / 8) % NT == 0, "epilogue rows");
 };
 
@@ -66,6 +74,14 @@ __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 // (vmcnt) before it, and each wave drains its own LDS accesses (lgkmcnt) so no buffer is
 // refilled or reread under a pending access; the epilogue's global stores need not drain.
 __device__ __forceinline__ void block_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Wait until at most N of this wave's vector memory operations are outstanding. They
+// complete in issue order, so this means every load issued before the last N has landed.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Byte offset, inside one stage's A or B region, of logical 16-byte chunk c of row r.
 __device__ __forceinline__ int lds_off(int r, int c) { return (r * 8 + (c ^ swz(r))) * 16; }
@@ -85,18 +101,18 @@ __device__ __forceinline__ uint32_t scale_base(uint32_t r, uint32_t nblk4) {
 template <int LAYOUT>
 constexpr uint32_t scale_step() { return LAYOUT == 0 ? 4u : 512u; }
 
-template <int BM, int BN, int WMW, int WNW, int A_LAYOUT, int B_LAYOUT>
-__global__ __launch_bounds__(WMW * WNW * 64, 1) void gemm_kernel(
+template <class T, int A_LAYOUT, int B_LAYOUT>
+__global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, uint16_t* __restrict__ C, int M, int N, int K, int ldc, int num_chunks,
     int first_chunk, int* __restrict__ chunk_done, int wide_store) {
-  using T = Tile<BM, BN, WMW, WNW>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * T::STAGE];
+  constexpr int BM = T::BM, BN = T::BN, NS = T::NS;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave / WNW, wn = wave % WNW;
+  const int wm = wave / (BN / T::WTN), wn = wave % (BN / T::WTN);
   const int l32 = lane & 31, g = lane >> 5;
 
   const int chunk_rows = M / num_chunks;
@@ -141,7 +157,9 @@ __global__ __launch_bounds__(WMW * WNW * 64, 1) void gemm_kernel(
     }
 #pragma unroll
     for (int i = 0; i < T::DS; ++i) {
-      const int row = (wave * T::DS + i) * 64 + lane;  // A rows, then B rows
+      // A rows first, then B rows; with fewer than 64 rows per wave the upper lanes repeat
+      // the wave's last row (same source, same LDS slot contents).
+      const int row = wave * T::SROWS + i * 64 + min(lane, T::SROWS - 1);
       if (row < BM) {
         s_src[i] = As;
         s_off[i] = scale_base<A_LAYOUT>((uint32_t)min(m0 + row, M - 1), nblk4);
@@ -153,8 +171,8 @@ __global__ __launch_bounds__(WMW * WNW * 64, 1) void gemm_kernel(
       }
     }
 
-    auto issue = [&](int kt) {
-      uint8_t* st = smem + (kt & 1) * T::STAGE;
+    auto issue = [&](int kt, int buf) {
+      uint8_t* st = smem + buf * T::STAGE;
       const uint32_t k0 = (uint32_t)kt * BK;
 #pragma unroll
       for (int i = 0; i < T::DA; ++i)
@@ -165,10 +183,20 @@ __global__ __launch_bounds__(WMW * WNW * 64, 1) void gemm_kernel(
         __builtin_amdgcn_global_load_lds((const void*)(B + b_off[i] + k0),
                                          (lds_void*)(st + T::A_BYTES + (wave * T::DB + i) * 1024), 16, 0, 0);
 #pragma unroll
-      for (int i = 0; i < T::DS; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(s_src[i] + s_off[i] + (uint32_t)kt * s_step[i]),
-                                         (lds_void*)(st + T::A_BYTES + T::B_BYTES + (wave * T::DS + i) * 256),
-                                         4, 0, 0);
+      for (int i = 0; i < T::DS; ++i) {
+        if (T::SROWS >= 64) {
+          __builtin_amdgcn_global_load_lds((const void*)(s_src[i] + s_off[i] + (uint32_t)kt * s_step[i]),
+                                           (lds_void*)(st + T::A_BYTES + T::B_BYTES + (wave * T::SROWS + i * 64) * 4),
+                                           4, 0, 0);
+        } else {
+          // fewer rows than lanes: the surplus lanes write past this wave's slice, so they
+          // are masked off (the instruction still counts once in vmcnt for the wave)
+          if (lane < T::SROWS)
+            __builtin_amdgcn_global_load_lds((const void*)(s_src[i] + s_off[i] + (uint32_t)kt * s_step[i]),
+                                             (lds_void*)(st + T::A_BYTES + T::B_BYTES + wave * T::SROWS * 4),
+                                             4, 0, 0);
+        }
+      }
     };
 
     v16f acc[T::TN][T::TM];
@@ -180,14 +208,23 @@ __global__ __launch_bounds__(WMW * WNW * 64, 1) void gemm_kernel(
         for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.f;
 
     block_barrier();  // the previous tile's epilogue is done with LDS
-    issue(0);
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < KT) issue(s, s);
+    int buf = 0;                // buffer of stage kt
+    int fill = NS - 1;          // buffer that stage kt + NS - 1 goes to
     for (int kt = 0; kt < KT; ++kt) {
-      // this stage's loads have landed in LDS for every wave; the other buffer is free
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // stage kt has landed in LDS for every wave; up to NS - 2 later stages stay in flight
+      if (kt + NS - 2 < KT)
+        wait_vm<(NS - 2) * T::LOADS>();
+      else
+        wait_vm<0>();
       block_barrier();
-      if (kt + 1 < KT) issue(kt + 1);
+      if (kt + NS - 1 < KT) issue(kt + NS - 1, fill);  // refills the buffer read at step kt - 1
+      fill = fill + 1 == NS ? 0 : fill + 1;
 
-      const uint8_t* st = smem + (kt & 1) * T::STAGE;
+      const uint8_t* st = smem + buf * T::STAGE;
+      buf = buf + 1 == NS ? 0 : buf + 1;
       const uint8_t* a_lds = st;
       const uint8_t* b_lds = st + T::A_BYTES;
       const uint32_t* sc = (const uint32_t*)(st + T::A_BYTES + T::B_BYTES);
@@ -274,52 +311,88 @@ __global__ __launch_bounds__(WMW * WNW * 64, 1) void gemm_kernel(
   }
 }
 
-constexpr int TILE_M = 256, TILE_N = 256, WAVES_M = 4, WAVES_N = 2;
+// Tile configurations: output tile, wave grid, LDS stages.
+using TileL = Tile<256, 256, 4, 2, 2>;  // 8 waves of 64 x 128; large problems
+using TileM = Tile<128, 128, 4, 2, 4>;  // 8 waves of 32 x 64
+using TileS = Tile<64, 128, 2, 4, 4>;   // 8 waves of 32 x 32
+using TileT = Tile<32, 128, 1, 4, 4>;   // 4 waves of 32 x 32; a few rows per chunk
+
+constexpr int REF_CUS = 256;  // compute units the tile choice is made for (MI355X)
 
 int device_cu_count() {
   static std::atomic<int> cached[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return REF_CUS;
   int v = cached[dev].load(std::memory_order_relaxed);
   if (v > 0) return v;
   int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = REF_CUS;
   cached[dev].store(n, std::memory_order_relaxed);
   return n;
+}
+
+int64_t tile_count(int64_t m, int64_t n, int num_chunks, int bm, int bn) {
+  return (int64_t)num_chunks * ((m / num_chunks + bm - 1) / bm) * ((n + bn - 1) / bn);
+}
+
+enum { CFG_L, CFG_M, CFG_S, CFG_T };
+
+// The largest tile that fits a chunk's rows and still gives about three quarters of the
+// compute units a tile: a 256 x 256 tile keeps the most data reuse per LDS byte, the smaller
+// ones trade that for more workgroups and more stages in flight when there are few tiles.
+int pick_config(int64_t m, int64_t n, int num_chunks) {
+  const int64_t rows = m / num_chunks;
+  const int64_t want = 3 * REF_CUS / 4;
+  if (rows >= TileL::BM && tile_count(m, n, num_chunks, TileL::BM, TileL::BN) >= want) return CFG_L;
+  if (rows >= TileM::BM && tile_count(m, n, num_chunks, TileM::BM, TileM::BN) >= want) return CFG_M;
+  if (rows >= TileS::BM && tile_count(m, n, num_chunks, TileS::BM, TileS::BN) >= want) return CFG_S;
+  return CFG_T;
+}
+
+template <class T>
+hipError_t launch_cfg(const uint8_t* a, const uint8_t* as, int a_layout, const uint8_t* b, const uint8_t* bs,
+                      int b_layout, int64_t m, int64_t n, int64_t k, uint16_t* c, int64_t ldc, int num_chunks,
+                      int first_chunk, int* chunk_done, hipStream_t stream) {
+  const int64_t tiles = tile_count(m, n, num_chunks, T::BM, T::BN);
+  const int64_t grid = tiles < device_cu_count() ? tiles : device_cu_count();
+  const int wide = ((uintptr_t)c % 16 == 0 && ldc % 8 == 0) ? 1 : 0;
+  const dim3 g((unsigned)grid), blk(T::NT);
+  const int M = (int)m, N = (int)n, K = (int)k, L = (int)ldc;
+  if (a_layout == 0 && b_layout == 0)
+    gemm_kernel<T, 0, 0><<<g, blk, 0, stream>>>(a, as, b, bs, c, M, N, K, L, num_chunks, first_chunk, chunk_done, wide);
+  else if (a_layout == 0 && b_layout == 1)
+    gemm_kernel<T, 0, 1><<<g, blk, 0, stream>>>(a, as, b, bs, c, M, N, K, L, num_chunks, first_chunk, chunk_done, wide);
+  else if (a_layout == 1 && b_layout == 0)
+    gemm_kernel<T, 1, 0><<<g, blk, 0, stream>>>(a, as, b, bs, c, M, N, K, L, num_chunks, first_chunk, chunk_done, wide);
+  else
+    gemm_kernel<T, 1, 1><<<g, blk, 0, stream>>>(a, as, b, bs, c, M, N, K, L, num_chunks, first_chunk, chunk_done, wide);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 GemmShape gemm_pick_shape(int64_t m, int64_t n, int num_chunks) {
-  (void)m;
-  (void)n;
-  (void)num_chunks;
-  return GemmShape{TILE_M, TILE_N};
+  switch (pick_config(m, n, num_chunks)) {
+    case CFG_L: return GemmShape{TileL::BM, TileL::BN};
+    case CFG_M: return GemmShape{TileM::BM, TileM::BN};
+    case CFG_S: return GemmShape{TileS::BM, TileS::BN};
+    default: return GemmShape{TileT::BM, TileT::BN};
+  }
 }
 
 hipError_t launch_gemm(const uint8_t* a, const uint8_t* as, int a_layout, const uint8_t* b,
                        const uint8_t* bs, int b_layout, int64_t m, int64_t n, int64_t k, uint16_t* c,
                        int64_t ldc, int num_chunks, int first_chunk, int* chunk_done, hipStream_t stream) {
-  const int64_t chunk_rows = m / num_chunks;
-  const int64_t tiles = (int64_t)num_chunks * ((chunk_rows + TILE_M - 1) / TILE_M) * ((n + TILE_N - 1) / TILE_N);
-  const int64_t grid = tiles < device_cu_count() ? tiles : device_cu_count();
-  const int wide = ((uintptr_t)c % 16 == 0 && ldc % 8 == 0) ? 1 : 0;
-  const dim3 g((unsigned)grid), blk(WAVES_M * WAVES_N * 64);
-  const int M = (int)m, N = (int)n, K = (int)k, L = (int)ldc;
-#define MXFP8_GEMM_LAUNCH(AL, BL)                                                                   \
-  gemm_kernel<TILE_M, TILE_N, WAVES_M, WAVES_N, AL, BL><<<g, blk, 0, stream>>>(a, as, b, bs, c, M, N, K, L, \
-                                                                               num_chunks, first_chunk, \
-                                                                               chunk_done, wide)
-  if (a_layout == 0 && b_layout == 0)
-    MXFP8_GEMM_LAUNCH(0, 0);
-  else if (a_layout == 0 && b_layout == 1)
-    MXFP8_GEMM_LAUNCH(0, 1);
-  else if (a_layout == 1 && b_layout == 0)
-    MXFP8_GEMM_LAUNCH(1, 0);
-  else
-    MXFP8_GEMM_LAUNCH(1, 1);
-#undef MXFP8_GEMM_LAUNCH
-  return hipGetLastError();
+  switch (pick_config(m, n, num_chunks)) {
+    case CFG_L:
+      return launch_cfg<TileL>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
+    case CFG_M:
+      return launch_cfg<TileM>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
+    case CFG_S:
+      return launch_cfg<TileS>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
+    default:
+      return launch_cfg<TileT>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
+  }
 }
 
 }  // namespace mxfp8

@@ -93,6 +93,24 @@ def test_gemm_small_full(m, n, k, chunks, la, lb):
     _assert_close(c, ref, _abs_sum_full(qa, sa[la], la, qb, sb[lb], lb), f"m={m} n={n} k={k}")
 
 
+# One shape per tile configuration (the kernel picks the tile from the rows per chunk and the
+# tile count), each with ragged M and N tails: (m, n, k, chunks, tile_m, tile_n).
+TILE_CASES = [(1000, 12200, 256, 1, 256, 256), (200, 12250, 256, 1, 128, 128),
+              (100, 12200, 256, 1, 64, 128), (132, 6100, 256, 4, 32, 128)]
+
+
+@pytest.mark.parametrize("la,lb", [(0, 1), (1, 0)])
+@pytest.mark.parametrize("m,n,k,chunks,tm,tn", TILE_CASES)
+def test_gemm_tile_configs_full(m, n, k, chunks, tm, tn, la, lb):
+    print(f"gemm tile config {tm}x{tn}: m={m} n={n} k={k} chunks={chunks} layouts={la}{lb}", flush=True)
+    rows = m // chunks
+    assert mx.gemm_tiles_per_chunk(m, n, chunks) == -(-rows // tm) * -(-n // tn)
+    qa, sa, qb, sb = _operands(m, n, k, seed_a=m + 1, seed_b=n + 1)
+    ref = oracle.gemm(qa, sa[la], la, qb, sb[lb], lb)
+    c = _gpu_gemm(qa, sa[la], la, qb, sb[lb], lb, num_chunks=chunks, first_chunk=chunks - 1)
+    _assert_close(c, ref, _abs_sum_full(qa, sa[la], la, qb, sb[lb], lb), f"tile {tm}x{tn} m={m} n={n}")
+
+
 def test_gemm_o_proj_m128_full():
     """o_proj, M=128, K=2048, N=6144, linear scales, compared in full."""
     qa, sa, qb, sb = _operands(128, N_MODEL, 2048)
