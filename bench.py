@@ -42,7 +42,33 @@ def _parse():
     p.add_argument("--sweep", action="store_true", help="per-shape GEMM/quantiser lines instead of the step")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run one 1 GiB device-to-device copy first (the reference kernel that scales the "
+                        "FETCH_SIZE / WRITE_SIZE counters of a profiled run)")
     return p.parse_args()
+
+
+# HBM traffic of one launch of the K=3072 GEMM, from two rocprofv3 --pmc runs of this script
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by the factor that maps the
+# counter of a 1 GiB copy onto 1 GiB. Valid only for the kernel source it was taken on.
+GEMM_TRAFFIC = {
+    "source_sha256": "01f56673ef0a516a5d581add46452c60f9a63e105af32b223f5bce6575a5f872",
+    "fetch_kib": 456266.6, "write_kib": 393342.4,
+    "fetch_factor": 2.0, "write_factor": 1.0,
+}
+
+
+def gemm_traffic_bytes():
+    import hashlib
+    src = os.path.join(ROOT, "quant_mxfp8_gemm_amd", "csrc", "gemm.hip")
+    try:
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    t = GEMM_TRAFFIC
+    if t["source_sha256"] != sha or t["fetch_kib"] is None or t["write_kib"] is None:
+        return None
+    return int(round((t["fetch_kib"] * t["fetch_factor"] + t["write_kib"] * t["write_factor"]) * 1024))
 
 
 def gemm_bytes(m, n, k):
@@ -117,6 +143,13 @@ def main():
 
     if args.sweep:
         return sweep(args, mx, synth, torch, dev)
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- resident inputs (untimed): activations, norm input, pre-quantised weights
     x, w = synth.norm_inputs_bf16(NORM_ROWS, N_MODEL)
@@ -207,7 +240,8 @@ def main():
                    "m": M_CHAIN, "n": N_MODEL, "k": [K_DOWN, K_O], "num_chunks": CHUNKS,
                    "norm_rows": NORM_ROWS, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_FP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_FP8_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_FP8_TFLOPS, 4),
+                     "traffic": gemm_traffic_bytes(),
                      "kernel": "gemm 32768x6144x3072"},
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kernels.items()},
     }
