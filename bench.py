@@ -303,6 +303,14 @@ def sweep(args, mx, synth, torch, dev):
     gbs = norm_bytes(NORM_ROWS, N_MODEL) / med / 1e9
     print(json.dumps({"kind": "rmsnorm_quant", "rows": NORM_ROWS, "hidden": N_MODEL, "us_median": round(med * 1e6, 2),
                       "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}), flush=True)
+    # swizzle after a row gather: linear scales of the gathered activation -> 128x4 layout
+    for rows, k in ((NORM_ROWS, N_MODEL), (M_CHAIN, K_DOWN)):
+        s_lin = torch.randint(0, 256, (rows, k // 32), dtype=torch.uint8, device=dev)
+        s_out = torch.empty(mx.scale_bytes(rows, k, mx.SWIZZLED), dtype=torch.uint8, device=dev)
+        med, p10, p90 = timed(lambda: mx.swizzle_scales(s_lin, out=s_out), max(args.steps, 10))
+        gbs = (s_lin.numel() + s_out.numel()) / med / 1e9
+        print(json.dumps({"kind": "swizzle_scales", "rows": rows, "k": k, "us_median": round(med * 1e6, 2),
+                          "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}), flush=True)
 
 
 if __name__ == "__main__":

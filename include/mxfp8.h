@@ -1,10 +1,11 @@
 /*
  * mxfp8.h - C ABI of the MI355X (gfx950) MXFP8 library.
  *
- * Three operations, each one or two HIP kernels, all asynchronous on the
+ * Four operations, each one or two HIP kernels, all asynchronous on the
  * caller's stream:
  *   mxfp8_quantize        BF16 [rows,k] -> E4M3 [rows,k] + UE8M0 scales (one per 32 along k)
  *   rmsnorm_quant_mxfp8   Gemma RMSNorm fused with the same quantisation
+ *   mxfp8_swizzle_scales  linear scales -> 128x4 swizzled scales (after a gather)
  *   mxfp8_gemm_bf16out    C[m,n] = sum_k A[m,k] B[n,k] with per-32-K block scales, BF16 out,
  *                         written in M-row chunks (one chunk = one rank's reduce-scatter shard)
  *
@@ -110,6 +111,25 @@ int rmsnorm_quant_mxfp8(const void* x_bf16, const void* w_bf16, int64_t rows, in
 int rmsnorm_quant_mxfp8_check(const void* x_bf16, const void* w_bf16, int64_t rows, int64_t hidden,
                               int64_t ldx, const void* q_e4m3, const void* scales_linear,
                               const void* scales_swizzled);
+
+/*
+ * mxfp8_swizzle_scales - linear UE8M0 scales -> the 128x4 swizzled layout, the step after an
+ * all-gather of MXFP8 activations: swizzled scales cannot be concatenated by rows (PR #65496,
+ * "Tradeoff"), so the norm emits linear scales, ranks gather codes and linear scales (half the
+ * bytes of a BF16 gather), and the gathered scales are swizzled once before the GEMM.
+ *
+ *   scales_linear   [rows, k/32] UE8M0 bytes, row-major, any alignment.
+ *   rows >= 0, k > 0 with k % 32 == 0 (k is the element count per row; k/32 blocks).
+ *   scales_swizzled mxfp8_scale_bytes(rows, k, MXFP8_SCALES_SWIZZLED_128X4) bytes, 16-byte aligned;
+ *                   every byte is written (pad bytes 0). Must not overlap scales_linear.
+ *   rows == 0 is a no-op (pointers may be NULL).
+ */
+int mxfp8_swizzle_scales(const void* scales_linear, int64_t rows, int64_t k, void* scales_swizzled,
+                         hipStream_t stream);
+
+/* Host-side argument check of mxfp8_swizzle_scales (same rules, no HIP call). */
+int mxfp8_swizzle_scales_check(const void* scales_linear, int64_t rows, int64_t k,
+                               const void* scales_swizzled);
 
 /*
  * mxfp8_gemm_bf16out - the per-rank MXFP8 GEMM of the o_proj / down_proj GEMM-RS

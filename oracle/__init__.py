@@ -52,6 +52,8 @@ def _load():
     lib.oracle_swizzle_offset.argtypes = [i64, i64, i64]
     lib.oracle_scale_bytes.restype = i64
     lib.oracle_scale_bytes.argtypes = [i64, i64, ctypes.c_int]
+    lib.oracle_swizzle_scales.restype = ctypes.c_int
+    lib.oracle_swizzle_scales.argtypes = [c_u8p, i64, i64, c_u8p]
     lib.oracle_mxfp8_quantize.restype = ctypes.c_int
     lib.oracle_mxfp8_quantize.argtypes = [c_u16p, i64, i64, i64, c_u8p, c_u8p, c_u8p]
     lib.oracle_rmsnorm_quant_mxfp8.restype = ctypes.c_int
@@ -122,6 +124,18 @@ def swizzle_offset(r: int, c: int, nblk: int) -> int:
 
 def scale_bytes(rows: int, k: int, layout: int) -> int:
     return _load().oracle_scale_bytes(rows, k, layout)
+
+
+def swizzle_scales(s_lin: np.ndarray) -> np.ndarray:
+    """Linear scales [rows, k/32] u8 -> flat swizzled buffer (pad bytes 0)."""
+    lib = _load()
+    s = np.ascontiguousarray(s_lin, dtype=np.uint8)
+    rows, nblk = s.shape
+    out = np.empty(scale_bytes(rows, 32 * nblk, SWIZZLED), dtype=np.uint8)
+    if rows:
+        _check(lib.oracle_swizzle_scales(_ptr(s, ctypes.c_uint8), rows, 32 * nblk, _ptr(out, ctypes.c_uint8)),
+               "oracle_swizzle_scales")
+    return out
 
 
 def quantize(x_bits: np.ndarray, k: int = None):

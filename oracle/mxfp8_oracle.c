@@ -179,6 +179,23 @@ int64_t oracle_scale_bytes(int64_t rows, int64_t k, int layout) {
   return ((rows + 127) / 128) * 128 * ((nblk + 3) / 4) * 4;
 }
 
+/*
+ * Linear scales [rows, k/32] -> the swizzled layout, every other byte 0. The step a row-wise
+ * gather of MXFP8 activations needs before the GEMM: swizzled tiles mix 128 rows, so shards
+ * can only be concatenated while their scales are linear (vLLM PR #65496, "Tradeoff";
+ * PR #64659, "Details"). Each byte is moved on its own by the offset definition above.
+ */
+int oracle_swizzle_scales(const uint8_t* s_lin, int64_t rows, int64_t k, uint8_t* s_swz) {
+  if (rows < 0 || k <= 0 || k % 32 != 0) return ORACLE_EINVAL;
+  if (rows == 0) return ORACLE_OK;
+  if (!s_lin || !s_swz) return ORACLE_EINVAL;
+  int64_t nblk = k / 32;
+  memset(s_swz, 0, (size_t)oracle_scale_bytes(rows, k, 1));
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < nblk; ++c) s_swz[oracle_swizzle_offset(r, c, nblk)] = s_lin[r * nblk + c];
+  return ORACLE_OK;
+}
+
 static int64_t scale_index(int layout, int64_t r, int64_t c, int64_t nblk) {
   return layout == 0 ? r * nblk + c : oracle_swizzle_offset(r, c, nblk);
 }

@@ -1,4 +1,4 @@
-"""MI355X (gfx950) MXFP8 quantiser, fused Gemma RMSNorm quantiser and block-scaled GEMM.
+"""MI355X (gfx950) MXFP8 quantiser, fused Gemma RMSNorm quantiser, scale swizzle and block-scaled GEMM.
 
 A thin ctypes binding over ``libmxfp8_amd.so`` (C ABI: ``include/mxfp8.h``). Every step of
 the computation runs in the library's HIP kernels; this module only checks tensor
@@ -55,6 +55,10 @@ def load_library():
     lib.rmsnorm_quant_mxfp8.argtypes = [vp, vp, i64, i64, i64, f32, vp, vp, vp, vp]
     lib.rmsnorm_quant_mxfp8_check.restype = i32
     lib.rmsnorm_quant_mxfp8_check.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
+    lib.mxfp8_swizzle_scales.restype = i32
+    lib.mxfp8_swizzle_scales.argtypes = [vp, i64, i64, vp, vp]
+    lib.mxfp8_swizzle_scales_check.restype = i32
+    lib.mxfp8_swizzle_scales_check.argtypes = [vp, i64, i64, vp]
     lib.mxfp8_gemm_bf16out.restype = i32
     lib.mxfp8_gemm_bf16out.argtypes = [vp, vp, i32, vp, vp, i32, i64, i64, i64, vp, i64, i32, i32, vp, vp]
     lib.mxfp8_gemm_bf16out_check.restype = i32
@@ -145,6 +149,27 @@ def rmsnorm_quant(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, linear: b
     if st != OK:
         raise MXFP8Error("rmsnorm_quant_mxfp8", st)
     return q, s_lin, s_swz
+
+
+def swizzle_scales(scales_linear: torch.Tensor, k: int = None, out: torch.Tensor = None) -> torch.Tensor:
+    """Linear UE8M0 scales ``[rows, k/32]`` u8 -> the flat 128x4-swizzled buffer (pad bytes 0),
+    the step after gathering MXFP8 activations by rows. ``k`` defaults to 32 x the column count."""
+    _dev(scales_linear, "scales_linear")
+    if scales_linear.dtype != torch.uint8 or scales_linear.dim() != 2 or not scales_linear.is_contiguous():
+        raise ValueError("scales_linear must be a contiguous 2-D uint8 tensor")
+    rows, nblk = scales_linear.shape
+    k = 32 * nblk if k is None else int(k)
+    if k != 32 * nblk:
+        raise ValueError("k must be 32 x the number of scale columns")
+    if out is None:
+        out = torch.empty(scale_bytes(rows, k, SWIZZLED), dtype=torch.uint8, device=scales_linear.device)
+    _dev(out, "out")
+    if out.dtype != torch.uint8 or not out.is_contiguous() or out.numel() < scale_bytes(rows, k, SWIZZLED):
+        raise ValueError("out must be a contiguous uint8 tensor of scale_bytes(rows, k, SWIZZLED) bytes")
+    st = load_library().mxfp8_swizzle_scales(_ptr(scales_linear), rows, k, _ptr(out), _stream(scales_linear))
+    if st != OK:
+        raise MXFP8Error("mxfp8_swizzle_scales", st)
+    return out
 
 
 def gemm(a: torch.Tensor, a_scales: torch.Tensor, a_layout: int, b: torch.Tensor, b_scales: torch.Tensor,

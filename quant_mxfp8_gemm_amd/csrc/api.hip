@@ -77,6 +77,23 @@ int rmsnorm_quant_mxfp8(const void* x_bf16, const void* w_bf16, int64_t rows, in
                                                 (uint8_t*)scales_linear, (uint8_t*)scales_swizzled, stream));
 }
 
+int mxfp8_swizzle_scales_check(const void* scales_linear, int64_t rows, int64_t k,
+                               const void* scales_swizzled) {
+  if (rows < 0 || k <= 0 || k % 32 != 0) return MXFP8_EINVAL;
+  if (rows == 0) return MXFP8_OK;  // nothing to read or write
+  if (!scales_linear || !scales_swizzled) return MXFP8_EINVAL;
+  if (!aligned(scales_swizzled, 16)) return MXFP8_EALIGN;
+  return MXFP8_OK;
+}
+
+int mxfp8_swizzle_scales(const void* scales_linear, int64_t rows, int64_t k, void* scales_swizzled,
+                         hipStream_t stream) {
+  const int st = mxfp8_swizzle_scales_check(scales_linear, rows, k, scales_swizzled);
+  if (st != MXFP8_OK) return st;
+  return hip_status(mxfp8::launch_swizzle_scales((const uint8_t*)scales_linear, rows, k,
+                                                 (uint8_t*)scales_swizzled, stream));
+}
+
 int mxfp8_gemm_bf16out_check(const void* a_e4m3, const void* a_scales, int a_scale_layout,
                              const void* b_e4m3, const void* b_scales, int b_scale_layout,
                              int64_t m, int64_t n, int64_t k, const void* c_bf16, int64_t ldc,

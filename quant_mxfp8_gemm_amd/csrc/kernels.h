@@ -17,6 +17,9 @@ hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* w, int64_t ro
 // Zero the pad bytes of a swizzled scale buffer for a [rows, k] operand (no-op without padding).
 hipError_t launch_swizzle_pad_zero(uint8_t* s_swz, int64_t rows, int64_t k, hipStream_t stream);
 
+// Linear scales [rows, k/32] -> 128x4 swizzled layout with zero pad bytes.
+hipError_t launch_swizzle_scales(const uint8_t* lin, int64_t rows, int64_t k, uint8_t* swz, hipStream_t stream);
+
 struct GemmShape {
   int bm, bn;  // output tile
 };

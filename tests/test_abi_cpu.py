@@ -34,8 +34,8 @@ def lib():
 
 def test_header_declares_the_three_operations():
     names = _declared_functions()
-    for f in ("mxfp8_quantize", "rmsnorm_quant_mxfp8", "mxfp8_gemm_bf16out", "mxfp8_scale_bytes",
-              "mxfp8_status_string"):
+    for f in ("mxfp8_quantize", "rmsnorm_quant_mxfp8", "mxfp8_gemm_bf16out", "mxfp8_swizzle_scales",
+              "mxfp8_scale_bytes", "mxfp8_status_string"):
         assert f in names
 
 
@@ -89,6 +89,18 @@ def test_rmsnorm_check(lib):
     assert c(P, P + 2, 1024, 6144, 6144, P, P, P) == EALIGN
 
 
+def test_swizzle_check(lib):
+    c = lib.mxfp8_swizzle_scales_check
+    assert c(P, 1024, 6144, P) == OK
+    assert c(P + 1, 1024, 6144, P) == OK          # linear scales may sit at any byte
+    assert c(None, 0, 6144, None) == OK           # rows == 0: nothing is touched
+    assert c(P, 1024, 6150, P) == EINVAL          # k % 32
+    assert c(P, -1, 6144, P) == EINVAL
+    assert c(None, 1024, 6144, P) == EINVAL
+    assert c(P, 1024, 6144, None) == EINVAL
+    assert c(P, 1024, 6144, P + 8) == EALIGN      # output not 16-byte aligned
+
+
 def test_gemm_check(lib):
     c = lib.mxfp8_gemm_bf16out_check
     good = dict(a=P, sa=P, la=0, b=P, sb=P, lb=1, m=4096, n=6144, k=3072, c=P, ldc=6144, nc=4, fc=0)
@@ -121,3 +133,8 @@ def test_tiles_per_chunk(lib):
     t = mx.gemm_tiles_per_chunk(32768, 6144, 4)
     assert t > 0 and t * 4 * 256 * 256 >= 32768 * 6144
     assert lib.mxfp8_gemm_tiles_per_chunk(10, 10, 3) == -1
+    # the tile shrinks when a 256 x 256 tiling leaves the compute units idle
+    assert mx.gemm_tiles_per_chunk(32768, 6144, 4) == 32 * 24    # 256 x 256
+    assert mx.gemm_tiles_per_chunk(1024, 6144, 4) == 2 * 48      # 128 x 128
+    assert mx.gemm_tiles_per_chunk(256, 6144, 1) == 4 * 48       # 64 x 128
+    assert mx.gemm_tiles_per_chunk(128, 6144, 1) == 4 * 48       # 32 x 128

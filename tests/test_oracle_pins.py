@@ -287,6 +287,23 @@ def test_quantize_swizzled_equals_reshaped_linear(rows, k):
     assert np.array_equal(s_swz, _swizzle_by_reshape(s_lin))
 
 
+@pytest.mark.parametrize("rows,nblk", [(1, 1), (127, 5), (128, 4), (300, 96), (129, 64)])
+def test_swizzle_scales_equals_reshape(rows, nblk):
+    """oracle.swizzle_scales against the independent pad/reshape/transpose construction,
+    including pad rows, pad blocks and a buffer that starts non-zero."""
+    s = np.random.default_rng(rows * 7 + nblk).integers(1, 255, (rows, nblk), dtype=np.uint8)
+    assert np.array_equal(oracle.swizzle_scales(s), _swizzle_by_reshape(s))
+
+
+def test_swizzle_after_gather_equals_whole():
+    """Gathering linear scale shards by rows and swizzling once gives the swizzled scales of
+    the whole operand (the reason the gathered path carries linear scales)."""
+    x = _bf16_bits_from_f64(np.random.default_rng(11).standard_normal((320, 256)))
+    _, s_lin_whole, s_swz_whole = oracle.quantize(x)
+    shards = [oracle.quantize(x[i:i + 80])[1] for i in range(0, 320, 80)]
+    assert np.array_equal(oracle.swizzle_scales(np.concatenate(shards)), s_swz_whole)
+
+
 def test_quantize_row_stride():
     x = _bf16_bits_from_f64(np.random.default_rng(4).standard_normal((40, 160)))
     q_full, s_full, _ = oracle.quantize(np.ascontiguousarray(x[:, :96]))
