@@ -52,6 +52,10 @@ def _load():
     lib.oracle_swizzle_offset.argtypes = [i64, i64, i64]
     lib.oracle_scale_bytes.restype = i64
     lib.oracle_scale_bytes.argtypes = [i64, i64, ctypes.c_int]
+    lib.oracle_gemm_silu_mul_quant.restype = ctypes.c_int
+    lib.oracle_gemm_silu_mul_quant.argtypes = [c_u8p, c_u8p, ctypes.c_int, c_u8p, c_u8p, ctypes.c_int, i64, i64, i64,
+                                               ctypes.POINTER(ctypes.c_int64), i64, c_u8p, c_u8p,
+                                               ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_double)]
     lib.oracle_swizzle_scales.restype = ctypes.c_int
     lib.oracle_swizzle_scales.argtypes = [c_u8p, i64, i64, c_u8p]
     lib.oracle_mxfp8_quantize.restype = ctypes.c_int
@@ -124,6 +128,34 @@ def swizzle_offset(r: int, c: int, nblk: int) -> int:
 
 def scale_bytes(rows: int, k: int, layout: int) -> int:
     return _load().oracle_scale_bytes(rows, k, layout)
+
+
+def gemm_silu_mul_quant(a, a_scales, a_layout, w, w_scales, w_layout, rows=None, want_gu=False):
+    """Fused dense GEMM1: ``y = silu(A W_gate^T) * (A W_up^T)`` quantised per 32 along the
+    intermediate dimension. ``w`` is E4M3 ``[2*inter, k]`` (gate rows, then up rows).
+
+    ``rows`` (default: all) selects rows of ``a``; returns ``(q [nrows, inter] u8,
+    s_lin [nrows, inter/32] u8, y32 [nrows, inter] f32)`` plus the fp64 ``[nrows, 2*inter]``
+    gate/up values when ``want_gu``.
+    """
+    lib = _load()
+    a = np.ascontiguousarray(a, dtype=np.uint8)
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    sa = np.ascontiguousarray(a_scales, dtype=np.uint8)
+    sw = np.ascontiguousarray(w_scales, dtype=np.uint8)
+    m, k = a.shape
+    inter = w.shape[0] // 2
+    r = np.arange(m, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    q = np.empty((r.size, inter), dtype=np.uint8)
+    s_lin = np.empty((r.size, inter // 32), dtype=np.uint8)
+    y = np.empty((r.size, inter), dtype=np.float32)
+    gu = np.empty((r.size, 2 * inter), dtype=np.float64) if want_gu else None
+    _check(lib.oracle_gemm_silu_mul_quant(
+        _ptr(a, ctypes.c_uint8), _ptr(sa, ctypes.c_uint8), int(a_layout), _ptr(w, ctypes.c_uint8),
+        _ptr(sw, ctypes.c_uint8), int(w_layout), m, inter, k, r.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+        r.size, _ptr(q, ctypes.c_uint8), _ptr(s_lin, ctypes.c_uint8), y.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+        None if gu is None else gu.ctypes.data_as(ctypes.POINTER(ctypes.c_double))), "oracle_gemm_silu_mul_quant")
+    return (q, s_lin, y, gu) if want_gu else (q, s_lin, y)
 
 
 def swizzle_scales(s_lin: np.ndarray) -> np.ndarray:

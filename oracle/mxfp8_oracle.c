@@ -373,6 +373,58 @@ int oracle_mxfp8_gemm_sampled(const uint8_t* a, const uint8_t* as, int a_layout,
   return ORACLE_OK;
 }
 
+/* ------------------------------------ fused dense GEMM1: gate_up, SiLU-and-mul, quantiser */
+
+/*
+ * The dense MLP's first GEMM with its activation and quantisation fused, producing the MXFP8
+ * activation down_proj consumes (vLLM PR #65496, "Details: GEMM-RS with a quantized input":
+ * above the token threshold the fused dense GEMM1 hands down_proj an MXFP8 QuantizedActivation
+ * with swizzled scales). w: E4M3 [2*inter, k], rows [0, inter) the gate projection and rows
+ * [inter, 2*inter) the up projection. For each listed row r of a and each j < inter:
+ *   g = C[r, j], u = C[r, inter + j]          (exact values, as gemm_element above)
+ *   y = g / (1 + e^-g) * u                    (SiLU(g) times up, in fp64)
+ * y is rounded once to fp32 and that value is quantised per 32 along j as in the quantiser.
+ * Outputs are indexed by position t in rows[]: q [nrows, inter], s_lin [nrows, inter/32],
+ * y_out [nrows, inter] fp32 (optional), gu_out [nrows, 2*inter] fp64 g then u (optional).
+ */
+int oracle_gemm_silu_mul_quant(const uint8_t* a, const uint8_t* as, int a_layout, const uint8_t* w,
+                               const uint8_t* ws, int w_layout, int64_t m, int64_t inter, int64_t k,
+                               const int64_t* rows, int64_t nrows, uint8_t* q, uint8_t* s_lin,
+                               float* y_out, double* gu_out) {
+  if (m < 0 || inter <= 0 || inter % 32 != 0 || k <= 0 || k % 32 != 0 || nrows < 0) return ORACLE_EINVAL;
+  if (!a || !as || !w || !ws || !rows || !q || !s_lin) return ORACLE_EINVAL;
+  if ((a_layout != 0 && a_layout != 1) || (w_layout != 0 && w_layout != 1)) return ORACLE_EINVAL;
+  for (int64_t t = 0; t < nrows; ++t)
+    if (rows[t] < 0 || rows[t] >= m) return ORACLE_EINVAL;
+  init_tables();
+  init_values();
+  int64_t nblk = inter / 32;
+  int nomem = 0;
+#pragma omp parallel reduction(| : nomem)
+  {
+    double* y = (double*)malloc((size_t)inter * sizeof(double));
+    if (!y) nomem = 1;
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t t = 0; t < nrows; ++t) {
+      if (!y) continue;
+      for (int64_t j = 0; j < inter; ++j) {
+        double g = gemm_element(a, as, a_layout, w, ws, w_layout, rows[t], j, k);
+        double u = gemm_element(a, as, a_layout, w, ws, w_layout, rows[t], inter + j, k);
+        if (gu_out) {
+          gu_out[t * 2 * inter + j] = g;
+          gu_out[t * 2 * inter + inter + j] = u;
+        }
+        float y32 = (float)(g / (1.0 + exp(-g)) * u);
+        if (y_out) y_out[t * inter + j] = y32;
+        y[j] = (double)y32;
+      }
+      quantize_row(y, inter, q + t * inter, s_lin + t * nblk);
+    }
+    free(y);
+  }
+  return nomem ? ORACLE_ENOMEM : ORACLE_OK;
+}
+
 /* Threads an OpenMP region of this library uses. */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

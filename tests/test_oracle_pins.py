@@ -448,3 +448,103 @@ def test_gemm_swizzled_scales_and_sampling_agree():
     cols = rng.integers(0, n, 300)
     s_bf16, _ = oracle.gemm_sampled(a, sa, oracle.LINEAR, b, sb, oracle.LINEAR, rows, cols)
     assert np.array_equal(s_bf16, c_lin[rows, cols])
+
+
+# ----------------------------------------- fused dense GEMM1: gate_up, SiLU-and-mul, quantiser
+
+def _scale_exp(amax: float) -> int:
+    """Smallest e in [-127, 127] with amax <= 448 * 2^e, by exact power-of-two comparisons."""
+    if amax == 0.0:
+        return -127
+    e = math.ceil(math.log2(amax / 448.0))
+    while e < 127 and amax > math.ldexp(448.0, e):
+        e += 1
+    while e > -127 and amax <= math.ldexp(448.0, e - 1):
+        e -= 1
+    return max(-127, min(127, e))
+
+
+def _quantize_f32_rows(y32: np.ndarray):
+    """Independent per-32 quantisation of fp32 rows: python scale rule + torch's E4M3 cast."""
+    rows, n = y32.shape
+    s = np.empty((rows, n // 32), dtype=np.uint8)
+    q = np.empty((rows, n), dtype=np.uint8)
+    for r in range(rows):
+        for b in range(n // 32):
+            blk = y32[r, 32 * b:32 * b + 32].astype(np.float64)
+            e = _scale_exp(float(np.max(np.abs(blk))))
+            s[r, b] = e + 127
+            q[r, 32 * b:32 * b + 32] = _torch_e4m3_codes((blk * 2.0 ** -e).astype(np.float32))
+    return q, s
+
+
+def _silu_mul_f32(g: np.ndarray, u: np.ndarray) -> np.ndarray:
+    gt = torch.from_numpy(g.astype(np.float64))
+    return (torch.nn.functional.silu(gt) * torch.from_numpy(u.astype(np.float64))).to(torch.float32).numpy()
+
+
+def test_silu_mul_quant_closed_form():
+    """A = ones, so gate and up are k times one weight value each; y against torch's silu."""
+    inter, k = 64, 64
+    table = _torch_e4m3_values()
+    a = np.full((2, k), 0x38, np.uint8)                         # 1.0
+    sa = np.full((2, k // 32), 127, np.uint8)
+    rng = np.random.default_rng(21)
+    gate_codes = rng.integers(0, 0x7E, inter).astype(np.uint8) | (rng.integers(0, 2, inter) * 0x80).astype(np.uint8)
+    up_codes = rng.integers(0, 0x7E, inter).astype(np.uint8) | (rng.integers(0, 2, inter) * 0x80).astype(np.uint8)
+    w = np.concatenate([np.repeat(gate_codes[:, None], k, 1), np.repeat(up_codes[:, None], k, 1)])
+    sw = np.full((2 * inter, k // 32), 125, np.uint8)          # 2^-2
+    q, s_lin, y, gu = oracle.gemm_silu_mul_quant(a, sa, oracle.LINEAR, w, sw, oracle.LINEAR, want_gu=True)
+    g = k * table[gate_codes] * 0.25
+    u = k * table[up_codes] * 0.25
+    assert np.array_equal(gu[0, :inter], g) and np.array_equal(gu[0, inter:], u)
+    want_y = _silu_mul_f32(g, u)
+    assert np.array_equal(y[0], want_y) and np.array_equal(y[1], want_y)
+    want_q, want_s = _quantize_f32_rows(want_y[None, :])
+    assert np.array_equal(q[0], want_q[0]) and np.array_equal(s_lin[0], want_s[0])
+
+
+def test_silu_mul_quant_brute_force():
+    """Random codes and scales: decode, matmul, silu and quantise outside the oracle."""
+    m, inter, k = 6, 96, 128
+    rng = np.random.default_rng(22)
+    table = _torch_e4m3_values()
+    a = rng.integers(0, 0x7E, (m, k)).astype(np.uint8) | (rng.integers(0, 2, (m, k)) * 0x80).astype(np.uint8)
+    w = rng.integers(0, 0x7E, (2 * inter, k)).astype(np.uint8) | (rng.integers(0, 2, (2 * inter, k)) * 0x80).astype(np.uint8)
+    sa = rng.integers(118, 130, (m, k // 32)).astype(np.uint8)
+    sw = rng.integers(118, 130, (2 * inter, k // 32)).astype(np.uint8)
+    a_deq = table[a] * np.exp2(np.repeat(sa.astype(np.int64) - 127, 32, axis=1))
+    w_deq = table[w] * np.exp2(np.repeat(sw.astype(np.int64) - 127, 32, axis=1))
+    c = np.matmul(a_deq, w_deq.T)
+    want_y = _silu_mul_f32(c[:, :inter], c[:, inter:])
+    q, s_lin, y = oracle.gemm_silu_mul_quant(a, _swizzle_by_reshape(sa), oracle.SWIZZLED, w, sw, oracle.LINEAR)
+    # the matmul sums in another order: fp32 y may differ by one unit in the last place
+    yi, wi = y.view(np.int32).astype(np.int64), want_y.view(np.int32).astype(np.int64)
+    assert np.all(np.abs(yi - wi) <= 1)
+    same = yi == wi
+    assert same.mean() > 0.9
+    want_q, want_s = _quantize_f32_rows(y)
+    assert np.array_equal(q, want_q) and np.array_equal(s_lin, want_s)
+    q2, s2 = _quantize_f32_rows(want_y)
+    assert np.array_equal(q[same], q2[same])
+
+
+def test_silu_mul_quant_special_rows_and_selection():
+    """Zero gate gives zero output (code 0 scales); a huge negative gate gives SiLU ~ 0;
+    selecting rows returns exactly those rows of the full result."""
+    inter, k = 32, 32
+    a = np.full((3, k), 0x38, np.uint8)
+    sa = np.full((3, 1), 127, np.uint8)
+    sa[2, 0] = 127 + 8                                          # row 2: A = 256
+    w = np.zeros((2 * inter, k), np.uint8)
+    w[inter:] = 0x38                                            # up = k * a
+    sw = np.full((2 * inter, 1), 127, np.uint8)
+    q, s_lin, y = oracle.gemm_silu_mul_quant(a, sa, oracle.LINEAR, w, sw, oracle.LINEAR)
+    assert np.all(y == 0) and np.all(s_lin == 0) and np.all((q & 0x7F) == 0)
+    w[:inter] = 0xFE                                            # gate weight -448: gate = -448 k a
+    q, s_lin, y = oracle.gemm_silu_mul_quant(a, sa, oracle.LINEAR, w, sw, oracle.LINEAR)
+    g = -448.0 * k * np.array([1.0, 1.0, 256.0])
+    want = _silu_mul_f32(np.repeat(g[:, None], inter, 1), np.repeat((k * np.array([1.0, 1.0, 256.0]))[:, None], inter, 1))
+    assert np.array_equal(y, want) and np.all(y <= 0)
+    qs, ss, ys = oracle.gemm_silu_mul_quant(a, sa, oracle.LINEAR, w, sw, oracle.LINEAR, rows=[2, 0])
+    assert np.array_equal(qs, q[[2, 0]]) and np.array_equal(ss, s_lin[[2, 0]]) and np.array_equal(ys, y[[2, 0]])
