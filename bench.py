@@ -303,6 +303,22 @@ def sweep(args, mx, synth, torch, dev):
     gbs = norm_bytes(NORM_ROWS, N_MODEL) / med / 1e9
     print(json.dumps({"kind": "rmsnorm_quant", "rows": NORM_ROWS, "hidden": N_MODEL, "us_median": round(med * 1e6, 2),
                       "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}), flush=True)
+    # fused dense GEMM1: gate_up [2 * 3072, 6144] GEMM + SiLU(gate) * up + MXFP8 quantisation
+    inter, hidden = K_DOWN, N_MODEL
+    wq_gu, _, ws_gu = mx.quantize(synth.weights_bf16(2 * inter, hidden, seed=1).to(dev), linear=False)
+    for m in (1024, 4096, 32768):
+        qa, _, sa = mx.quantize(synth.activations_bf16(m, hidden, seed=0).to(dev), linear=False)
+        out = (torch.empty((m, inter), dtype=torch.uint8, device=dev), None,
+               torch.empty(mx.scale_bytes(m, inter, mx.SWIZZLED), dtype=torch.uint8, device=dev))
+        for _ in range(args.warmup):
+            mx.gemm_silu_mul_quant(qa, sa, mx.SWIZZLED, wq_gu, ws_gu, mx.SWIZZLED, out=out)
+        med, p10, p90 = timed(lambda: mx.gemm_silu_mul_quant(qa, sa, mx.SWIZZLED, wq_gu, ws_gu, mx.SWIZZLED, out=out),
+                              max(args.steps, 10))
+        tf = 2.0 * m * 2 * inter * hidden / med / 1e12
+        print(json.dumps({"kind": "gemm_silu_mul_quant", "m": m, "n": 2 * inter, "k": hidden,
+                          "us_median": round(med * 1e6, 2), "us_p10": round(p10 * 1e6, 2), "us_p90": round(p90 * 1e6, 2),
+                          "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / PEAK_MFMA_FP8_TFLOPS, 4)}), flush=True)
+        del qa, sa, out
     # swizzle after a row gather: linear scales of the gathered activation -> 128x4 layout
     for rows, k in ((NORM_ROWS, N_MODEL), (M_CHAIN, K_DOWN)):
         s_lin = torch.randint(0, 256, (rows, k // 32), dtype=torch.uint8, device=dev)

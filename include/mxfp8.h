@@ -1,13 +1,15 @@
 /*
  * mxfp8.h - C ABI of the MI355X (gfx950) MXFP8 library.
  *
- * Four operations, each one or two HIP kernels, all asynchronous on the
+ * Five operations, each one or two HIP kernels, all asynchronous on the
  * caller's stream:
  *   mxfp8_quantize        BF16 [rows,k] -> E4M3 [rows,k] + UE8M0 scales (one per 32 along k)
  *   rmsnorm_quant_mxfp8   Gemma RMSNorm fused with the same quantisation
  *   mxfp8_swizzle_scales  linear scales -> 128x4 swizzled scales (after a gather)
  *   mxfp8_gemm_bf16out    C[m,n] = sum_k A[m,k] B[n,k] with per-32-K block scales, BF16 out,
  *                         written in M-row chunks (one chunk = one rank's reduce-scatter shard)
+ *   mxfp8_gemm_silu_mul_quant  the dense MLP's gate_up GEMM with SiLU(gate) * up and the MXFP8
+ *                         quantisation fused: MXFP8 in, MXFP8 (E4M3 + UE8M0) out
  *
  * Formats (vLLM PR #64659 "Details: GEMM-RS with a quantized input"; PR #65496 "Details"):
  *   E4M3  OCP OFP8 "FN": bias 7, max 448, no infinities, S.1111.111 NaN.
@@ -166,6 +168,36 @@ int mxfp8_gemm_bf16out_check(const void* a_e4m3, const void* a_scales, int a_sca
                              const void* b_e4m3, const void* b_scales, int b_scale_layout,
                              int64_t m, int64_t n, int64_t k, const void* c_bf16, int64_t ldc,
                              int num_chunks, int first_chunk);
+
+/*
+ * mxfp8_gemm_silu_mul_quant - the fused dense GEMM1: the gate_up projection, SiLU(gate) * up and
+ * the MXFP8 quantisation of the result in one kernel, so down_proj receives an MXFP8 activation
+ * with swizzled scales instead of a BF16 tensor it would quantise itself (PR #65496, "Details:
+ * GEMM-RS with a quantized input"; PR #64111, "Claims": fused dense GEMM1).
+ *   g[m,j] = C[m,j], u[m,j] = C[m,inter+j] with C as for mxfp8_gemm_bf16out (fp32 accumulation),
+ *   y[m,j] = g / (1 + e^-g) * u in fp32 from the accumulators (no BF16 rounding in between),
+ *   y quantised per 32 along j exactly as mxfp8_quantize does with an fp32 input.
+ *
+ *   a_e4m3 / a_scales  [m, k] E4M3 (dense, 16-byte aligned), scales in a_scale_layout (4-byte aligned).
+ *   w_e4m3 / w_scales  [2*inter, k] E4M3: rows [0, inter) the gate projection, rows [inter, 2*inter)
+ *                      the up projection (the merged gate_up weight); scales in w_scale_layout.
+ *   m >= 1; inter >= 32 with inter % 32 == 0; k > 0 with k % 32 == 0 (else MXFP8_EINVAL) and
+ *   k % 128 == 0 (else MXFP8_EUNSUPPORTED).
+ *   q_e4m3          [m, inter] E4M3, dense, 16-byte aligned.
+ *   scales_linear   [m, inter/32] or NULL; scales_swizzled mxfp8_scale_bytes(m, inter, SWIZZLED)
+ *                   bytes or NULL (pad bytes written 0); at least one non-NULL.
+ * Results do not depend on the tile configuration the library picks.
+ */
+int mxfp8_gemm_silu_mul_quant(const void* a_e4m3, const void* a_scales, int a_scale_layout,
+                              const void* w_e4m3, const void* w_scales, int w_scale_layout, int64_t m,
+                              int64_t inter, int64_t k, void* q_e4m3, void* scales_linear,
+                              void* scales_swizzled, hipStream_t stream);
+
+/* Host-side argument check of mxfp8_gemm_silu_mul_quant (same rules, no HIP call). */
+int mxfp8_gemm_silu_mul_quant_check(const void* a_e4m3, const void* a_scales, int a_scale_layout,
+                                    const void* w_e4m3, const void* w_scales, int w_scale_layout,
+                                    int64_t m, int64_t inter, int64_t k, const void* q_e4m3,
+                                    const void* scales_linear, const void* scales_swizzled);
 
 /* Output tiles per chunk that mxfp8_gemm_bf16out uses for this shape (the final value of
  * each chunk_done counter); -1 for invalid arguments. Host-only. */

@@ -63,6 +63,10 @@ def load_library():
     lib.mxfp8_gemm_bf16out.argtypes = [vp, vp, i32, vp, vp, i32, i64, i64, i64, vp, i64, i32, i32, vp, vp]
     lib.mxfp8_gemm_bf16out_check.restype = i32
     lib.mxfp8_gemm_bf16out_check.argtypes = [vp, vp, i32, vp, vp, i32, i64, i64, i64, vp, i64, i32, i32]
+    lib.mxfp8_gemm_silu_mul_quant.restype = i32
+    lib.mxfp8_gemm_silu_mul_quant.argtypes = [vp, vp, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp, vp]
+    lib.mxfp8_gemm_silu_mul_quant_check.restype = i32
+    lib.mxfp8_gemm_silu_mul_quant_check.argtypes = [vp, vp, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp]
     lib.mxfp8_gemm_tiles_per_chunk.restype = i64
     lib.mxfp8_gemm_tiles_per_chunk.argtypes = [i64, i64, i32]
     _lib = lib
@@ -206,3 +210,34 @@ def gemm(a: torch.Tensor, a_scales: torch.Tensor, a_layout: int, b: torch.Tensor
     if st != OK:
         raise MXFP8Error("mxfp8_gemm_bf16out", st)
     return out
+
+
+def gemm_silu_mul_quant(a: torch.Tensor, a_scales: torch.Tensor, a_layout: int, w: torch.Tensor,
+                        w_scales: torch.Tensor, w_layout: int, linear: bool = False, swizzled: bool = True,
+                        out=None):
+    """Fused dense GEMM1: ``y = SiLU(A W_gate^T) * (A W_up^T)`` quantised to MXFP8.
+
+    ``a`` E4M3 ``[m, k]`` u8, ``w`` E4M3 ``[2*inter, k]`` u8 (gate rows, then up rows), both
+    contiguous, scales in the given layouts. Returns ``(q [m, inter] u8, scales_linear,
+    scales_swizzled)``; ``out`` may pass them preallocated.
+    """
+    for t, nm in ((a, "a"), (w, "w"), (a_scales, "a_scales"), (w_scales, "w_scales")):
+        _dev(t, nm)
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous uint8 tensor")
+    if a.dim() != 2 or w.dim() != 2 or a.shape[1] != w.shape[1] or w.shape[0] % 2 != 0:
+        raise ValueError("a must be [m, k] and w [2*inter, k]")
+    m, k = a.shape
+    inter = w.shape[0] // 2
+    if out is not None:
+        q, s_lin, s_swz = out
+    else:
+        q = torch.empty((m, inter), dtype=torch.uint8, device=a.device)
+        s_lin = torch.empty((m, inter // 32), dtype=torch.uint8, device=a.device) if linear else None
+        s_swz = torch.empty(scale_bytes(m, inter, SWIZZLED), dtype=torch.uint8, device=a.device) if swizzled else None
+    st = load_library().mxfp8_gemm_silu_mul_quant(_ptr(a), _ptr(a_scales), int(a_layout), _ptr(w), _ptr(w_scales),
+                                                  int(w_layout), m, inter, k, _ptr(q), _ptr(s_lin), _ptr(s_swz),
+                                                  _stream(a))
+    if st != OK:
+        raise MXFP8Error("mxfp8_gemm_silu_mul_quant", st)
+    return q, s_lin, s_swz

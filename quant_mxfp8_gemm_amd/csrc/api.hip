@@ -128,6 +128,39 @@ int mxfp8_gemm_bf16out(const void* a_e4m3, const void* a_scales, int a_scale_lay
                                        stream));
 }
 
+int mxfp8_gemm_silu_mul_quant_check(const void* a_e4m3, const void* a_scales, int a_scale_layout,
+                                    const void* w_e4m3, const void* w_scales, int w_scale_layout, int64_t m,
+                                    int64_t inter, int64_t k, const void* q_e4m3, const void* scales_linear,
+                                    const void* scales_swizzled) {
+  if (m < 1 || inter < 32 || inter % 32 != 0 || k <= 0 || k % 32 != 0) return MXFP8_EINVAL;
+  if (!a_e4m3 || !a_scales || !w_e4m3 || !w_scales || !q_e4m3 || (!scales_linear && !scales_swizzled))
+    return MXFP8_EINVAL;
+  if ((a_scale_layout != MXFP8_SCALES_LINEAR && a_scale_layout != MXFP8_SCALES_SWIZZLED_128X4) ||
+      (w_scale_layout != MXFP8_SCALES_LINEAR && w_scale_layout != MXFP8_SCALES_SWIZZLED_128X4))
+    return MXFP8_EINVAL;
+  if (k % 128 != 0) return MXFP8_EUNSUPPORTED;
+  if (m * k > kMaxOperandBytes || 2 * inter * k > kMaxOperandBytes || m * inter > ((int64_t)1 << 40) ||
+      m > ((int64_t)1 << 30) || inter > ((int64_t)1 << 29))
+    return MXFP8_EUNSUPPORTED;
+  if (!aligned(a_e4m3, 16) || !aligned(w_e4m3, 16) || !aligned(a_scales, 4) || !aligned(w_scales, 4) ||
+      !aligned(q_e4m3, 16))
+    return MXFP8_EALIGN;
+  return MXFP8_OK;
+}
+
+int mxfp8_gemm_silu_mul_quant(const void* a_e4m3, const void* a_scales, int a_scale_layout, const void* w_e4m3,
+                              const void* w_scales, int w_scale_layout, int64_t m, int64_t inter, int64_t k,
+                              void* q_e4m3, void* scales_linear, void* scales_swizzled, hipStream_t stream) {
+  const int st = mxfp8_gemm_silu_mul_quant_check(a_e4m3, a_scales, a_scale_layout, w_e4m3, w_scales,
+                                                 w_scale_layout, m, inter, k, q_e4m3, scales_linear,
+                                                 scales_swizzled);
+  if (st != MXFP8_OK) return st;
+  return hip_status(mxfp8::launch_gemm_silu_mul_quant(
+      (const uint8_t*)a_e4m3, (const uint8_t*)a_scales, a_scale_layout, (const uint8_t*)w_e4m3,
+      (const uint8_t*)w_scales, w_scale_layout, m, inter, k, (uint8_t*)q_e4m3, (uint8_t*)scales_linear,
+      (uint8_t*)scales_swizzled, stream));
+}
+
 int64_t mxfp8_gemm_tiles_per_chunk(int64_t m, int64_t n, int num_chunks) {
   if (m < 1 || n < 1 || num_chunks < 1 || m % num_chunks != 0) return -1;
   const mxfp8::GemmShape s = mxfp8::gemm_pick_shape(m, n, num_chunks);

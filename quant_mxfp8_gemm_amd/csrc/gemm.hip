@@ -101,11 +101,21 @@ __device__ __forceinline__ uint32_t scale_base(uint32_t r, uint32_t nblk4) {
 template <int LAYOUT>
 constexpr uint32_t scale_step() { return LAYOUT == 0 ? 4u : 512u; }
 
-template <class T, int A_LAYOUT, int B_LAYOUT>
+// Outputs of the fused dense GEMM1 epilogue (EPI_SWIGLU): B holds 2*inter rows, gate then up.
+struct SwiGluOut {
+  uint8_t* q;      // [M, inter] E4M3
+  uint8_t* s_lin;  // [M, inter/32] or null
+  uint8_t* s_swz;  // swizzled [M, inter/32] or null
+  int inter;
+};
+
+enum { EPI_BF16 = 0, EPI_SWIGLU = 1 };
+
+template <class T, int A_LAYOUT, int B_LAYOUT, int EPI>
 __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, uint16_t* __restrict__ C, int M, int N, int K, int ldc, int num_chunks,
-    int first_chunk, int* __restrict__ chunk_done, int wide_store) {
+    int first_chunk, int* __restrict__ chunk_done, int wide_store, SwiGluOut sg) {
   constexpr int BM = T::BM, BN = T::BN, NS = T::NS;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
 
@@ -116,7 +126,10 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
   const int l32 = lane & 31, g = lane >> 5;
 
   const int chunk_rows = M / num_chunks;
-  const int tiles_n = (N + BN - 1) / BN;
+  // EPI_SWIGLU: a tile's BN columns are BN/2 gate columns j0.. and the BN/2 up columns of the
+  // same j, so SiLU(gate) * up of an output element is formed inside one tile
+  constexpr int HB = BN / 2;
+  const int tiles_n = EPI == EPI_SWIGLU ? (sg.inter + HB - 1) / HB : (N + BN - 1) / BN;
   const int tiles_mc = (chunk_rows + BM - 1) / BM;
   const int tpc = tiles_mc * tiles_n;
   const int total = tpc * num_chunks;
@@ -137,7 +150,13 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
     const int chunk_m0 = chunk * chunk_rows;
     const int m0 = chunk_m0 + tm_idx * BM;
     const int m_end = min(m0 + BM, chunk_m0 + chunk_rows);
-    const int n0 = tn_idx * BN;
+    const int n0 = tn_idx * (EPI == EPI_SWIGLU ? HB : BN);  // first output column (j0 for EPI_SWIGLU)
+    // B row that feeds tile column r (clamped into the operand; surplus columns are not stored)
+    auto b_row = [&](int r) -> uint32_t {
+      if (EPI == EPI_SWIGLU)
+        return r < HB ? (uint32_t)min(n0 + r, sg.inter - 1) : (uint32_t)(sg.inter + min(n0 + r - HB, sg.inter - 1));
+      return (uint32_t)min(n0 + r, N - 1);
+    };
 
     // ---- per-lane LDS-DMA sources (rows clamped into the operand; surplus rows are not stored)
     uint32_t a_off[T::DA], b_off[T::DB], s_off[T::DS];
@@ -153,7 +172,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
     for (int i = 0; i < T::DB; ++i) {
       const int s = (wave * T::DB + i) * 64 + lane;
       const int r = s >> 3;
-      b_off[i] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)K + (((s & 7) ^ swz(r)) * 16);
+      b_off[i] = b_row(r) * (uint32_t)K + (((s & 7) ^ swz(r)) * 16);
     }
 #pragma unroll
     for (int i = 0; i < T::DS; ++i) {
@@ -166,7 +185,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
         s_step[i] = scale_step<A_LAYOUT>();
       } else {
         s_src[i] = Bs;
-        s_off[i] = scale_base<B_LAYOUT>((uint32_t)min(n0 + row - BM, N - 1), nblk4);
+        s_off[i] = scale_base<B_LAYOUT>(b_row(row - BM), nblk4);
         s_step[i] = scale_step<B_LAYOUT>();
       }
     }
@@ -263,6 +282,72 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
       }
     }
 
+    if (EPI == EPI_SWIGLU) {
+      // ---- fused epilogue: fp32 gate and up staged in LDS a band of rows at a time, then one
+      // (row, 32-block of j) per thread: y = SiLU(g) * u, UE8M0 scale from amax, E4M3 codes
+      constexpr int SROW = BN * 4 + 16;  // bytes per staged row (gate floats, then up floats)
+      constexpr int FIT = T::LDS_BYTES / SROW / 32 * 32;
+      constexpr int PR = FIT < BM ? FIT : BM;  // rows per band
+      static_assert(PR >= 32 && BM % PR == 0 && T::WTM % 32 == 0, "fused epilogue bands");
+      constexpr int BPR = HB / 32;  // 32-blocks of j per tile row
+      const int nblk = sg.inter / 32;
+      const int64_t col_tiles = (nblk + 3) / 4;
+#pragma unroll
+      for (int p0 = 0; p0 < BM; p0 += PR) {
+        block_barrier();  // the stages (or the previous band) are no longer read
+#pragma unroll
+        for (int y = 0; y < T::TM; ++y) {
+          const int rb = wm * T::WTM + y * 32;
+          if (rb < p0 || rb >= p0 + PR) continue;
+          const int r = rb - p0 + l32;
+#pragma unroll
+          for (int x = 0; x < T::TN; ++x)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int c = wn * T::WTN + x * 32 + 8 * q + 4 * g;
+              *(float4*)(smem + r * SROW + c * 4) =
+                  make_float4(acc[x][y][4 * q + 0], acc[x][y][4 * q + 1], acc[x][y][4 * q + 2], acc[x][y][4 * q + 3]);
+            }
+        }
+        block_barrier();
+        for (int it = tid; it < PR * BPR; it += T::NT) {
+          const int r = it / BPR, b = it % BPR;
+          const int m = m0 + p0 + r;
+          const int j = n0 + 32 * b;
+          if (m >= m_end || j >= sg.inter) continue;
+          const float* gp = (const float*)(smem + r * SROW) + 32 * b;
+          const float* up = gp + HB;
+          float yv[32];
+          uint32_t amax = 0;
+#pragma unroll
+          for (int e = 0; e < 32; e += 4) {
+            const float4 g4 = *(const float4*)(gp + e);
+            const float4 u4 = *(const float4*)(up + e);
+            const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+            const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const float v = gg[t] / (1.0f + expf(-gg[t])) * uu[t];
+              yv[e + t] = v;
+              amax = max(amax, __float_as_uint(v) & 0x7FFFFFFFu);
+            }
+          }
+          const uint32_t code = ue8m0_from_amax_f32_bits(amax);
+          const float inv = inv_scale_from_ue8m0(code);
+          uint32_t w[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            w[t] = cvt_e4m3x4(yv[4 * t] * inv, yv[4 * t + 1] * inv, yv[4 * t + 2] * inv, yv[4 * t + 3] * inv);
+          uint8_t* qd = sg.q + (int64_t)m * sg.inter + j;
+          __builtin_nontemporal_store((u32x4){w[0], w[1], w[2], w[3]}, (u32x4*)qd);
+          __builtin_nontemporal_store((u32x4){w[4], w[5], w[6], w[7]}, (u32x4*)(qd + 16));
+          if (sg.s_lin) sg.s_lin[(int64_t)m * nblk + j / 32] = (uint8_t)code;
+          if (sg.s_swz) sg.s_swz[swizzled_offset(m, j / 32, col_tiles)] = (uint8_t)code;
+        }
+      }
+      continue;  // next tile (the fused output has no chunk counters)
+    }
+
     // ---- epilogue: BF16 tile staged in LDS, then full-line 16-byte stores
     block_barrier();  // every wave is done reading the last stage
 #pragma unroll
@@ -349,23 +434,23 @@ int pick_config(int64_t m, int64_t n, int num_chunks) {
   return CFG_T;
 }
 
-template <class T>
+template <class T, int EPI = EPI_BF16>
 hipError_t launch_cfg(const uint8_t* a, const uint8_t* as, int a_layout, const uint8_t* b, const uint8_t* bs,
                       int b_layout, int64_t m, int64_t n, int64_t k, uint16_t* c, int64_t ldc, int num_chunks,
-                      int first_chunk, int* chunk_done, hipStream_t stream) {
+                      int first_chunk, int* chunk_done, hipStream_t stream, SwiGluOut sg = SwiGluOut{}) {
   const int64_t tiles = tile_count(m, n, num_chunks, T::BM, T::BN);
   const int64_t grid = tiles < device_cu_count() ? tiles : device_cu_count();
   const int wide = ((uintptr_t)c % 16 == 0 && ldc % 8 == 0) ? 1 : 0;
   const dim3 g((unsigned)grid), blk(T::NT);
   const int M = (int)m, N = (int)n, K = (int)k, L = (int)ldc;
   if (a_layout == 0 && b_layout == 0)
-    gemm_kernel<T, 0, 0><<<g, blk, 0, stream>>>(a, as, b, bs, c, M, N, K, L, num_chunks, first_chunk, chunk_done, wide);
+    gemm_kernel<T, 0, 0, EPI><<<g, blk, 0, stream>>>(a, as, b, bs, c, M, N, K, L, num_chunks, first_chunk, chunk_done, wide, sg);
   else if (a_layout == 0 && b_layout == 1)
-    gemm_kernel<T, 0, 1><<<g, blk, 0, stream>>>(a, as, b, bs, c, M, N, K, L, num_chunks, first_chunk, chunk_done, wide);
+    gemm_kernel<T, 0, 1, EPI><<<g, blk, 0, stream>>>(a, as, b, bs, c, M, N, K, L, num_chunks, first_chunk, chunk_done, wide, sg);
   else if (a_layout == 1 && b_layout == 0)
-    gemm_kernel<T, 1, 0><<<g, blk, 0, stream>>>(a, as, b, bs, c, M, N, K, L, num_chunks, first_chunk, chunk_done, wide);
+    gemm_kernel<T, 1, 0, EPI><<<g, blk, 0, stream>>>(a, as, b, bs, c, M, N, K, L, num_chunks, first_chunk, chunk_done, wide, sg);
   else
-    gemm_kernel<T, 1, 1><<<g, blk, 0, stream>>>(a, as, b, bs, c, M, N, K, L, num_chunks, first_chunk, chunk_done, wide);
+    gemm_kernel<T, 1, 1, EPI><<<g, blk, 0, stream>>>(a, as, b, bs, c, M, N, K, L, num_chunks, first_chunk, chunk_done, wide, sg);
   return hipGetLastError();
 }
 
@@ -378,6 +463,23 @@ GemmShape gemm_pick_shape(int64_t m, int64_t n, int num_chunks) {
     case CFG_S: return GemmShape{TileS::BM, TileS::BN};
     default: return GemmShape{TileT::BM, TileT::BN};
   }
+}
+
+hipError_t launch_gemm_silu_mul_quant(const uint8_t* a, const uint8_t* as, int a_layout, const uint8_t* w,
+                                      const uint8_t* ws, int w_layout, int64_t m, int64_t inter, int64_t k,
+                                      uint8_t* q, uint8_t* s_lin, uint8_t* s_swz, hipStream_t stream) {
+  const SwiGluOut sg{q, s_lin, s_swz, (int)inter};
+  const int64_t n = 2 * inter;  // B rows; tile counts match whenever inter is a multiple of BN/2
+  hipError_t e;
+  switch (pick_config(m, n, 1)) {
+    case CFG_L: e = launch_cfg<TileL, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
+    case CFG_M: e = launch_cfg<TileM, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
+    case CFG_S: e = launch_cfg<TileS, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
+    default: e = launch_cfg<TileT, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
+  }
+  if (e != hipSuccess) return e;
+  if (s_swz) e = launch_swizzle_pad_zero(s_swz, m, inter, stream);
+  return e;
 }
 
 hipError_t launch_gemm(const uint8_t* a, const uint8_t* as, int a_layout, const uint8_t* b,

@@ -31,4 +31,9 @@ hipError_t launch_gemm(const uint8_t* a, const uint8_t* as, int a_layout, const 
                        const uint8_t* bs, int b_layout, int64_t m, int64_t n, int64_t k, uint16_t* c,
                        int64_t ldc, int num_chunks, int first_chunk, int* chunk_done, hipStream_t stream);
 
+// Fused dense GEMM1: gate_up GEMM (w = [gate; up], 2*inter rows), SiLU(gate) * up, MXFP8 quantisation.
+hipError_t launch_gemm_silu_mul_quant(const uint8_t* a, const uint8_t* as, int a_layout, const uint8_t* w,
+                                      const uint8_t* ws, int w_layout, int64_t m, int64_t inter, int64_t k,
+                                      uint8_t* q, uint8_t* s_lin, uint8_t* s_swz, hipStream_t stream);
+
 }  // namespace mxfp8

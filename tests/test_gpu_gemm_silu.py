@@ -1,0 +1,108 @@
+"""GPU parity of the fused dense GEMM1 (mxfp8_gemm_silu_mul_quant: gate_up MXFP8 GEMM, SiLU(gate)
+* up, per-32 MXFP8 quantisation) against the oracle.
+
+Inputs are quantised by the oracle on the CPU. The kernel forms gate and up in the MFMA's fp32
+accumulators, whose error is bounded by MFMA_MASS_ERR times the dot product's absolute mass, so
+its quantisation decisions may differ from the oracle's exact ones only within that bound: every
+scale must be reachable from an amax within the bound, every dequantised code must be a correct
+rounding of a value within the bound, and the share of decisions that differ must stay small.
+The oracle's own codes and scales are compared exactly where the comparison is decided. Small
+shapes (one per tile configuration, ragged rows and columns) are checked in full; the workload
+(M = 32768 tokens, inter = 3072 per rank, hidden K = 6144) on whole sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quant_mxfp8_gemm_amd as mx
+import synth
+from parity_util import bits16, dev_u8, guard_intact, guarded_u8, silu_mul_quant_check
+
+pytestmark = pytest.mark.gpu
+
+
+def _operands(m, inter, k, seed_a=0, seed_w=1):
+    a = synth.activations_bf16(m, k, seed=seed_a)
+    w = synth.weights_bf16(2 * inter, k, seed=seed_w)
+    qa, sa_lin, sa_swz = oracle.quantize(bits16(a))
+    qw, sw_lin, sw_swz = oracle.quantize(bits16(w))
+    return qa, {mx.LINEAR: sa_lin, mx.SWIZZLED: sa_swz}, qw, {mx.LINEAR: sw_lin, mx.SWIZZLED: sw_swz}
+
+
+def _run(qa, sa, la, qw, sw, lw):
+    m = qa.shape[0]
+    inter = qw.shape[0] // 2
+    qbuf, q = guarded_u8(m * inter)
+    lbuf, s_lin = guarded_u8(m * (inter // 32))
+    zbuf, s_swz = guarded_u8(mx.scale_bytes(m, inter, mx.SWIZZLED))
+    mx.gemm_silu_mul_quant(dev_u8(qa), dev_u8(sa), la, dev_u8(qw), dev_u8(sw), lw,
+                           out=(q.view(m, inter), s_lin.view(m, inter // 32), s_swz))
+    torch.cuda.synchronize()
+    assert guard_intact(qbuf) and guard_intact(lbuf) and guard_intact(zbuf), "write outside an output"
+    return q.view(m, inter).cpu().numpy(), s_lin.view(m, inter // 32).cpu().numpy(), s_swz.cpu().numpy()
+
+
+def _mass(qa, sa, la, qw, sw, lw, rows):
+    """sum_k |a_mk w_nk| for the listed rows and every column of the gate_up product."""
+    n = qw.shape[0]
+    ri = np.repeat(np.asarray(rows, dtype=np.int64), n)
+    ci = np.tile(np.arange(n, dtype=np.int64), len(rows))
+    _, f = oracle.gemm_sampled(qa & 0x7F, sa, la, qw & 0x7F, sw, lw, ri, ci)
+    return f.reshape(len(rows), n)
+
+
+# (m, inter, k, tile_m): one case per tile configuration, with ragged rows and columns
+CASES = [(2048, 3072, 256, 256), (1000, 1536, 256, 128), (100, 6112, 256, 64), (40, 1056, 256, 32)]
+
+
+@pytest.mark.parametrize("la,lw", [(1, 1), (0, 1)])
+@pytest.mark.parametrize("m,inter,k,tile_m", CASES)
+def test_gemm_silu_mul_quant_full(m, inter, k, tile_m, la, lw):
+    print(f"gemm_silu_mul_quant m={m} inter={inter} k={k} tile_m={tile_m} layouts={la}{lw}", flush=True)
+    qa, sa, qw, sw = _operands(m, inter, k, seed_a=m, seed_w=inter)
+    q, s_lin, s_swz = _run(qa, sa[la], la, qw, sw[lw], lw)
+    q_ref, s_ref, _, gu = oracle.gemm_silu_mul_quant(qa, sa[la], la, qw, sw[lw], lw, want_gu=True)
+    mass = _mass(qa, sa[la], la, qw, sw[lw], lw, range(m))
+    s_diff, v_diff = silu_mul_quant_check(q, s_lin, gu, mass, inter)
+    print(f"  scales differing {s_diff:.2e}, values differing {v_diff:.2e}", flush=True)
+    assert s_diff <= 0.01 and v_diff <= 0.01
+    # both layouts carry the same scales; pad bytes are zero
+    assert np.array_equal(s_swz, oracle.swizzle_scales(s_lin))
+    # where the kernel's scale agrees with the oracle's, most codes are the oracle's codes
+    assert np.mean(q == q_ref) > 0.99 and np.mean(s_lin == s_ref) > 0.99
+
+
+def test_gemm_silu_mul_quant_workload_rows():
+    """M = 32768, inter = 3072, K = 6144 (the dense MLP per TP4 rank feeding down_proj K = 3072)."""
+    m, inter, k = 32768, 3072, 6144
+    print(f"gemm_silu_mul_quant workload m={m} inter={inter} k={k}", flush=True)
+    qa, sa, qw, sw = _operands(m, inter, k)
+    q, s_lin, s_swz = _run(qa, sa[1], 1, qw, sw[1], 1)
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 8191, 8192, 16384, 32767],
+                                     rng.integers(0, m, 30)])).astype(np.int64)
+    q_ref, s_ref, _, gu = oracle.gemm_silu_mul_quant(qa, sa[1], 1, qw, sw[1], 1, rows=rows, want_gu=True)
+    mass = _mass(qa, sa[1], 1, qw, sw[1], 1, rows)
+    s_diff, v_diff = silu_mul_quant_check(q[rows], s_lin[rows], gu, mass, inter)
+    print(f"  scales differing {s_diff:.2e}, values differing {v_diff:.2e}", flush=True)
+    assert s_diff <= 0.01 and v_diff <= 0.01
+    assert np.mean(q[rows] == q_ref) > 0.99
+    # the swizzled scales of the sampled rows sit where the 128x4 layout puts them
+    nblk = inter // 32
+    for r in rows[:8]:
+        offs = [oracle.swizzle_offset(int(r), c, nblk) for c in range(nblk)]
+        assert np.array_equal(s_swz[offs], s_lin[r])
+
+
+def test_gemm_silu_mul_quant_feeds_down_proj():
+    """The fused output is a valid down_proj operand: the GEMM on it equals the GEMM on the
+    same codes with scales rebuilt from the linear copy."""
+    m, inter, k = 512, 1024, 512
+    qa, sa, qw, sw = _operands(m, inter, k)
+    q, s_lin, s_swz = mx.gemm_silu_mul_quant(dev_u8(qa), dev_u8(sa[1]), 1, dev_u8(qw), dev_u8(sw[1]), 1,
+                                             linear=True, swizzled=True)
+    wd, _, wds = mx.quantize(synth.weights_bf16(768, inter, seed=3).cuda(), linear=False)
+    c1 = mx.gemm(q, s_swz, mx.SWIZZLED, wd, wds, mx.SWIZZLED, num_chunks=4)
+    c2 = mx.gemm(q, s_lin, mx.LINEAR, wd, wds, mx.SWIZZLED, num_chunks=4)
+    torch.cuda.synchronize()
+    assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
