@@ -23,11 +23,13 @@
 //    B (output columns n) is fed as the first operand and A as the second, so each lane
 //    holds runs of 4 consecutive n of one output row m.
 //  * K advances 128 bytes per stage (one full 128-byte line per row). The stages of A, B and
-//    their scale dwords live in LDS and are filled by LDS-DMA loads (global_load_lds, 16 bytes
-//    per lane for data, 4 for scales) straight from memory. A row of a stage is 8 chunks of
-//    16 bytes; chunk c of row r sits in slot c ^ ((r ^ (r >> 3)) & 7), so the rows read by one
-//    ds_read_b128 spread over all banks. The 4 scale bytes of a row for one stage are one
-//    aligned dword in both scale layouts.
+//    their scale dwords live in LDS and are filled straight from memory by LDS-DMA loads:
+//    buffer_load_dwordx4 ... lds for A and B (a 32-bit row offset per lane, the stage's K
+//    offset in a scalar register), global_load_lds_dword for the scales. Each load
+//    instruction moves 8 whole rows (8 lanes per 128-byte line). A row of a stage is 8
+//    chunks of 16 bytes; chunk c of row r sits in slot c ^ ((r ^ (r >> 3)) & 7), so the rows
+//    read by one ds_read_b128 spread over all banks. The 4 scale bytes of a row for one
+//    stage are one aligned dword in both scale layouts.
 //  * Epilogue: the tile is converted to BF16 into LDS (over the stage buffers, rows padded by
 //    16 bytes) and written back with 16-byte streaming stores, every row a run of full lines.
 #include <atomic>
@@ -85,6 +87,15 @@ __device__ __forceinline__ void wait_vm() {
 
 // Byte offset, inside one stage's A or B region, of logical 16-byte chunk c of row r.
 __device__ __forceinline__ int lds_off(int r, int c) { return (r * 8 + (c ^ swz(r))) * 16; }
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// Raw buffer resource over [p, p + bytes) (gfx9 descriptor word 3); loads past the end read 0.
+// Device pass only: the host pass of this toolchain drops the kernel stubs when the
+// resource type appears in a kernel body, so the buffer code is compiled for the GPU alone.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+#endif
 
 template <int SEL>
 __device__ __forceinline__ v16f mfma(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
@@ -193,14 +204,19 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
     auto issue = [&](int kt, int buf) {
       uint8_t* st = smem + buf * T::STAGE;
       const uint32_t k0 = (uint32_t)kt * BK;
+#if defined(__HIP_DEVICE_COMPILE__)
+      // A and B through buffer resources: per-lane 32-bit row offsets, the K offset of the
+      // stage in a scalar register
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K);
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(B, (uint32_t)N * (uint32_t)K);
 #pragma unroll
       for (int i = 0; i < T::DA; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(A + a_off[i] + k0),
-                                         (lds_void*)(st + (wave * T::DA + i) * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + (wave * T::DA + i) * 1024), 16, a_off[i], k0, 0, 0);
 #pragma unroll
       for (int i = 0; i < T::DB; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(B + b_off[i] + k0),
-                                         (lds_void*)(st + T::A_BYTES + (wave * T::DB + i) * 1024), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + T::A_BYTES + (wave * T::DB + i) * 1024), 16,
+                                                 b_off[i], k0, 0, 0);
+#endif
 #pragma unroll
       for (int i = 0; i < T::DS; ++i) {
         if (T::SROWS >= 64) {
