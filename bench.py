@@ -52,8 +52,8 @@ def _parse():
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by the factor that maps the
 # counter of a 1 GiB copy onto 1 GiB. Valid only for the kernel source it was taken on.
 GEMM_TRAFFIC = {
-    "source_sha256": "01f56673ef0a516a5d581add46452c60f9a63e105af32b223f5bce6575a5f872",
-    "fetch_kib": 456266.6, "write_kib": 393342.4,
+    "source_sha256": "1d9e97f64f68167cd6865076dbc760c1bd9a6d4c0bf65978f514dd1c31ae8fff",
+    "fetch_kib": 456265.1, "write_kib": 393595.3,
     "fetch_factor": 2.0, "write_factor": 1.0,
 }
 
@@ -319,6 +319,24 @@ def sweep(args, mx, synth, torch, dev):
                           "us_median": round(med * 1e6, 2), "us_p10": round(p10 * 1e6, 2), "us_p90": round(p90 * 1e6, 2),
                           "TFLOP/s": round(tf, 1), "frac_mfma": round(tf / PEAK_MFMA_FP8_TFLOPS, 4)}), flush=True)
         del qa, sa, out
+    # the platform's own MXFP8 GEMM on the headline shape, for context: torch._scaled_mm with
+    # E8M0 block scales (served by hipBLASLt), same codes and scale values as this library's run
+    try:
+        m, k = M_CHAIN, K_DOWN
+        qa, sl, _ = mx.quantize(synth.activations_bf16(m, k, seed=0).to(dev), swizzled=False)
+        qb, tl, _ = mx.quantize(synth.weights_bf16(N_MODEL, k, seed=1).to(dev), swizzled=False)
+        fa, fb = qa.view(torch.float8_e4m3fn), qb.view(torch.float8_e4m3fn)
+        e8a, e8b = sl.view(torch.float8_e8m0fnu), tl.view(torch.float8_e8m0fnu)
+        vendor = lambda: torch._scaled_mm(fa, fb.t(), scale_a=e8a, scale_b=e8b, out_dtype=torch.bfloat16)
+        vendor()
+        med, p10, p90 = timed(vendor, max(args.steps, 10))
+        tf = 2.0 * m * N_MODEL * k / med / 1e12
+        print(json.dumps({"kind": "vendor_scaled_mm_mxfp8", "m": m, "n": N_MODEL, "k": k,
+                          "us_median": round(med * 1e6, 2), "TFLOP/s": round(tf, 1),
+                          "frac_mfma": round(tf / PEAK_MFMA_FP8_TFLOPS, 4)}), flush=True)
+        del qa, qb, sl, tl
+    except Exception as e:  # the vendor path is context only
+        print(json.dumps({"kind": "vendor_scaled_mm_mxfp8", "error": repr(e)[:200]}), flush=True)
     # swizzle after a row gather: linear scales of the gathered activation -> 128x4 layout
     for rows, k in ((NORM_ROWS, N_MODEL), (M_CHAIN, K_DOWN)):
         s_lin = torch.randint(0, 256, (rows, k // 32), dtype=torch.uint8, device=dev)
