@@ -35,7 +35,7 @@ def lib():
 def test_header_declares_the_three_operations():
     names = _declared_functions()
     for f in ("mxfp8_quantize", "rmsnorm_quant_mxfp8", "mxfp8_gemm_bf16out", "mxfp8_swizzle_scales",
-              "mxfp8_scale_bytes", "mxfp8_status_string"):
+              "mxfp8_gemm_silu_mul_quant", "mxfp8_scale_bytes", "mxfp8_status_string"):
         assert f in names
 
 
@@ -127,6 +127,31 @@ def test_gemm_check(lib):
     assert call(c=P + 4) == EALIGN
     assert call(ldc=6146) == EALIGN
     assert call(m=1 << 20, k=3072) == EUNSUP   # operand beyond 2 GiB
+
+
+def test_gemm_silu_mul_quant_check(lib):
+    c = lib.mxfp8_gemm_silu_mul_quant_check
+    good = dict(a=P, sa=P, la=1, w=P, sw=P, lw=1, m=32768, i=3072, k=6144, q=P, sl=None, sz=P)
+
+    def call(**kw):
+        d = dict(good)
+        d.update(kw)
+        return c(d["a"], d["sa"], d["la"], d["w"], d["sw"], d["lw"], d["m"], d["i"], d["k"], d["q"], d["sl"], d["sz"])
+
+    assert call() == OK
+    assert call(sl=P, sz=None) == OK
+    assert call(sl=None, sz=None) == EINVAL     # no scale output
+    assert call(m=0) == EINVAL
+    assert call(i=3000) == EINVAL              # inter % 32
+    assert call(i=0) == EINVAL
+    assert call(k=6150) == EINVAL              # k % 32
+    assert call(k=6176) == EUNSUP              # k % 128
+    assert call(la=3) == EINVAL
+    assert call(w=None) == EINVAL
+    assert call(q=P + 8) == EALIGN             # codes 16-byte aligned
+    assert call(a=P + 4) == EALIGN
+    assert call(sw=P + 2) == EALIGN
+    assert call(m=1 << 20, k=6144) == EUNSUP   # A beyond 2 GiB
 
 
 def test_tiles_per_chunk(lib):
