@@ -50,21 +50,32 @@ def _parse():
 
 # HBM traffic of one launch of the K=3072 GEMM, from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by the factor that maps the
-# counter of a 1 GiB copy onto 1 GiB. Valid only for the kernel source it was taken on.
+# counter of a 1 GiB copy onto 1 GiB. Valid only for the kernel code it was taken on
+# (gemm_code_sha256).
 GEMM_TRAFFIC = {
-    "source_sha256": "1d9e97f64f68167cd6865076dbc760c1bd9a6d4c0bf65978f514dd1c31ae8fff",
+    "source_sha256": "07b5efab8890ed455a28f321eb8c6fa8bba6d50e55b0ea28ee128915233d0b3a",
     "fetch_kib": 456265.1, "write_kib": 393595.3,
     "fetch_factor": 2.0, "write_factor": 1.0,
 }
 
 
-def gemm_traffic_bytes():
+def gemm_code_sha256():
+    """SHA-256 of gemm.hip with comments and whitespace removed: the kernel code the traffic
+    figures belong to (a comment edit does not invalidate them, a code edit does)."""
     import hashlib
+    import re
     src = os.path.join(ROOT, "quant_mxfp8_gemm_amd", "csrc", "gemm.hip")
     try:
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        text = open(src).read()
     except OSError:
         return None
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return hashlib.sha256("".join(text.split()).encode()).hexdigest()
+
+
+def gemm_traffic_bytes():
+    sha = gemm_code_sha256()
     t = GEMM_TRAFFIC
     if t["source_sha256"] != sha or t["fetch_kib"] is None or t["write_kib"] is None:
         return None

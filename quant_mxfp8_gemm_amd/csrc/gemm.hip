@@ -7,7 +7,7 @@
 // match one rank's reduce-scatter shard ("Overview", "Details").
 //
 // Design (CDNA4):
-//  * Persistent grid: one 8-wave workgroup per CU walks the output tiles in dispatch order.
+//  * Persistent grid: one workgroup per CU walks the output tiles in dispatch order.
 //    Tile order: chunk by chunk from first_chunk; inside a chunk every XCD (workgroups are
 //    placed round-robin over the 8 XCDs) gets a contiguous run of tiles, grouped GM tile-rows
 //    tall, so the 32 tiles an XCD works on at once share A and B panels in its L2.
@@ -32,6 +32,10 @@
 //    stage are one aligned dword in both scale layouts.
 //  * Epilogue: the tile is converted to BF16 into LDS (over the stage buffers, rows padded by
 //    16 bytes) and written back with 16-byte streaming stores, every row a run of full lines.
+//  * A second epilogue serves the fused dense GEMM1 (gate_up projection, SiLU(gate) * up,
+//    MXFP8 quantisation; vLLM PR #65496 "Details", PR #64111 "Claims"): a tile's columns are
+//    half gate and half up for the same output columns, the fp32 accumulators meet in LDS and
+//    each thread turns one (row, 32-block) into E4M3 codes and a UE8M0 scale.
 #include <atomic>
 
 #include "device_common.h"
