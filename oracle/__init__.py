@@ -52,6 +52,9 @@ def _load():
     lib.oracle_swizzle_offset.argtypes = [i64, i64, i64]
     lib.oracle_scale_bytes.restype = i64
     lib.oracle_scale_bytes.argtypes = [i64, i64, ctypes.c_int]
+    lib.oracle_add_rmsnorm_quant_mxfp8.restype = ctypes.c_int
+    lib.oracle_add_rmsnorm_quant_mxfp8.argtypes = [c_u16p, c_u16p, c_u16p, i64, i64, i64, i64, ctypes.c_double,
+                                                   c_u8p, c_u8p, c_u8p, c_u16p, ctypes.POINTER(ctypes.c_float)]
     lib.oracle_gemm_silu_mul_quant.restype = ctypes.c_int
     lib.oracle_gemm_silu_mul_quant.argtypes = [c_u8p, c_u8p, ctypes.c_int, c_u8p, c_u8p, ctypes.c_int, i64, i64, i64,
                                                ctypes.POINTER(ctypes.c_int64), i64, c_u8p, c_u8p,
@@ -202,6 +205,28 @@ def rmsnorm_quant(x_bits: np.ndarray, w_bits: np.ndarray, eps: float):
                                           float(eps), _ptr(q, ctypes.c_uint8), _ptr(s_lin, ctypes.c_uint8),
                                           _ptr(s_swz, ctypes.c_uint8), _ptr(y, ctypes.c_float)), "rmsnorm_quant")
     return q, s_lin, s_swz, y
+
+
+def add_rmsnorm_quant(x_bits: np.ndarray, r_bits: np.ndarray, w_bits: np.ndarray, eps: float):
+    """Residual add h = BF16(x + r), then Gemma RMSNorm + MXFP8 quantisation of h.
+    Returns (codes, linear scales, swizzled scales, h BF16 bits, y fp32)."""
+    lib = _load()
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    r = np.ascontiguousarray(r_bits, dtype=np.uint16)
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    rows, h = x.shape
+    assert r.shape == x.shape and w.shape == (h,)
+    q = np.empty((rows, h), dtype=np.uint8)
+    s_lin = np.empty((rows, h // 32), dtype=np.uint8)
+    s_swz = np.empty(scale_bytes(rows, h, SWIZZLED), dtype=np.uint8)
+    hb = np.empty((rows, h), dtype=np.uint16)
+    y = np.empty((rows, h), dtype=np.float32)
+    _check(lib.oracle_add_rmsnorm_quant_mxfp8(_ptr(x, ctypes.c_uint16), _ptr(r, ctypes.c_uint16),
+                                              _ptr(w, ctypes.c_uint16), rows, h, h, h, float(eps),
+                                              _ptr(q, ctypes.c_uint8), _ptr(s_lin, ctypes.c_uint8),
+                                              _ptr(s_swz, ctypes.c_uint8), _ptr(hb, ctypes.c_uint16),
+                                              _ptr(y, ctypes.c_float)), "add_rmsnorm_quant")
+    return q, s_lin, s_swz, hb, y
 
 
 def gemm(a, a_scales, a_layout, b, b_scales, b_layout, want_f64=False):

@@ -259,6 +259,32 @@ int oracle_mxfp8_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ld
 /* ------------------------------------------------- Gemma RMSNorm + quantiser */
 
 /*
+ * One row of the Gemma RMSNorm quantiser: y = x / sqrt(sum(x^2)/hidden + eps) * (1 + w) in
+ * fp64, rounded once to fp32, then quantised as above. y (double scratch of hidden values)
+ * and codes (hidden/32 bytes) are caller buffers. Returns 1 if x holds a non-finite value.
+ */
+static int norm_row(const uint16_t* xr, const uint16_t* w, int64_t hidden, double eps, uint8_t* q,
+                    uint8_t* codes, double* y, float* y_out) {
+  int bad = 0;
+  double ss = 0.0;
+  for (int64_t i = 0; i < hidden; ++i) {
+    double xi = oracle_bf16_value(xr[i]);
+    if (!isfinite(xi)) bad = 1;
+    ss += xi * xi;
+  }
+  double rstd = 1.0 / sqrt(ss / (double)hidden + eps);
+  for (int64_t i = 0; i < hidden; ++i) {
+    double xi = oracle_bf16_value(xr[i]);
+    double wi = oracle_bf16_value(w[i]);
+    float y32 = (float)(xi * rstd * (1.0 + wi));
+    if (y_out) y_out[i] = y32;
+    y[i] = (double)y32;
+  }
+  quantize_row(y, hidden, q, codes);
+  return bad;
+}
+
+/*
  * y = x / sqrt(sum(x^2)/hidden + eps) * (1 + w), in fp64, rounded once to fp32,
  * then quantised as above. x: BF16 [rows, hidden] (row stride ldx), w: BF16
  * [hidden]. y_out (optional): the fp32 y, [rows, hidden] dense.
@@ -278,25 +304,50 @@ int oracle_rmsnorm_quant_mxfp8(const uint16_t* x, const uint16_t* w, int64_t row
     uint8_t* codes = (uint8_t*)malloc((size_t)nblk);
     if (!y || !codes) nomem = 1;
 #pragma omp for schedule(static)
-  for (int64_t r = 0; r < rows; ++r) {
-    if (!y || !codes) continue;
-    double ss = 0.0;
-    for (int64_t i = 0; i < hidden; ++i) {
-      double xi = oracle_bf16_value(x[r * ldx + i]);
-      if (!isfinite(xi)) bad = 1;
-      ss += xi * xi;
+    for (int64_t r = 0; r < rows; ++r) {
+      if (!y || !codes) continue;
+      bad |= norm_row(x + r * ldx, w, hidden, eps, q + r * hidden, codes, y, y_out ? y_out + r * hidden : NULL);
+      store_scales(codes, r, nblk, s_lin, s_swz);
     }
-    double rstd = 1.0 / sqrt(ss / (double)hidden + eps);
-    for (int64_t i = 0; i < hidden; ++i) {
-      double xi = oracle_bf16_value(x[r * ldx + i]);
-      double wi = oracle_bf16_value(w[i]);
-      float y32 = (float)(xi * rstd * (1.0 + wi));
-      if (y_out) y_out[r * hidden + i] = y32;
-      y[i] = (double)y32;
-    }
-    quantize_row(y, hidden, q + r * hidden, codes);
-    store_scales(codes, r, nblk, s_lin, s_swz);
+    free(y);
+    free(codes);
   }
+  if (nomem) return ORACLE_ENOMEM;
+  return bad ? ORACLE_ENONFINITE : ORACLE_OK;
+}
+
+/*
+ * Residual add ahead of the norm: h = BF16(x + r) (the two BF16 values summed exactly and
+ * rounded once, to nearest even) is the new residual stream, and the norm above is applied
+ * to h. The pages fuse the norm and the quantisation with the all-reduce that produces x in
+ * decode (vLLM PR #64111, "Claims": all-reduce + Gemma norm + MXFP8 quant); on one GPU the
+ * all-reduced x is an input. x, r: BF16 [rows, hidden] with row strides ldx, ldr.
+ * h_out: BF16 bits [rows, hidden] dense (required); y_out optional as above.
+ */
+int oracle_add_rmsnorm_quant_mxfp8(const uint16_t* x, const uint16_t* r, const uint16_t* w, int64_t rows,
+                                   int64_t hidden, int64_t ldx, int64_t ldr, double eps, uint8_t* q,
+                                   uint8_t* s_lin, uint8_t* s_swz, uint16_t* h_out, float* y_out) {
+  if (rows < 0 || hidden <= 0 || hidden % 32 != 0 || ldx < hidden || ldr < hidden || !x || !r || !w || !q ||
+      !h_out)
+    return ORACLE_EINVAL;
+  init_tables();
+  int64_t nblk = hidden / 32;
+  if (s_swz) memset(s_swz, 0, (size_t)oracle_scale_bytes(rows, hidden, 1));
+  int bad = 0, nomem = 0;
+#pragma omp parallel reduction(| : bad, nomem)
+  {
+    double* y = (double*)malloc((size_t)hidden * sizeof(double));
+    uint8_t* codes = (uint8_t*)malloc((size_t)nblk);
+    if (!y || !codes) nomem = 1;
+#pragma omp for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+      if (!y || !codes) continue;
+      uint16_t* h = h_out + i * hidden;
+      for (int64_t j = 0; j < hidden; ++j)
+        h[j] = oracle_bf16_from_double(oracle_bf16_value(x[i * ldx + j]) + oracle_bf16_value(r[i * ldr + j]));
+      bad |= norm_row(h, w, hidden, eps, q + i * hidden, codes, y, y_out ? y_out + i * hidden : NULL);
+      store_scales(codes, i, nblk, s_lin, s_swz);
+    }
     free(y);
     free(codes);
   }

@@ -548,3 +548,47 @@ def test_silu_mul_quant_special_rows_and_selection():
     assert np.array_equal(y, want) and np.all(y <= 0)
     qs, ss, ys = oracle.gemm_silu_mul_quant(a, sa, oracle.LINEAR, w, sw, oracle.LINEAR, rows=[2, 0])
     assert np.array_equal(qs, q[[2, 0]]) and np.array_equal(ss, s_lin[[2, 0]]) and np.array_equal(ys, y[[2, 0]])
+
+
+# ------------------------------------------------- residual add + Gemma RMSNorm + quantiser
+
+def _add_inputs(rows, h, seed):
+    rng = np.random.default_rng(seed)
+    x = _bf16_bits_from_f64(rng.standard_normal((rows, h)) * np.exp2(rng.integers(-6, 6, (rows, 1))))
+    r = _bf16_bits_from_f64(rng.standard_normal((rows, h)) * 4.0)
+    w = _bf16_bits_from_f64(rng.standard_normal(h) * 0.1)
+    return x, r, w
+
+
+def test_add_rmsnorm_residual_matches_torch_bf16_add():
+    """h = BF16(x + r) against torch's fp32 add rounded to BF16 (exact sum, one rounding)."""
+    x, r, w = _add_inputs(40, 256, 41)
+    _, _, _, h, _ = oracle.add_rmsnorm_quant(x, r, w, EPS)
+    xt = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).float()
+    rt = torch.from_numpy(r.view(np.int16)).view(torch.bfloat16).float()
+    want = (xt + rt).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(h, want)
+
+
+def test_add_rmsnorm_is_norm_of_the_sum():
+    """The quantised output is the plain norm quantiser applied to h; with r = 0 it is the
+    norm quantiser applied to x."""
+    x, r, w = _add_inputs(24, 512, 42)
+    q, sl, ss, h, y = oracle.add_rmsnorm_quant(x, r, w, EPS)
+    q2, sl2, ss2, y2 = oracle.rmsnorm_quant(h, w, EPS)
+    assert np.array_equal(q, q2) and np.array_equal(sl, sl2) and np.array_equal(ss, ss2)
+    assert np.array_equal(y, y2)
+    zero = np.zeros_like(r)
+    q3, sl3, ss3, h3, _ = oracle.add_rmsnorm_quant(x, zero, w, EPS)
+    q4, sl4, ss4, _ = oracle.rmsnorm_quant(x, w, EPS)
+    assert np.array_equal(q3, q4) and np.array_equal(sl3, sl4) and np.array_equal(ss3, ss4)
+    assert np.array_equal(_bits_to_f64(h3), _bits_to_f64(x))
+
+
+def test_add_rmsnorm_cancelling_residual_gives_zero():
+    """r = -x: h = 0, y = 0, every code and scale is zero."""
+    x, _, w = _add_inputs(3, 64, 43)
+    r = x ^ np.uint16(0x8000)
+    q, sl, _, h, y = oracle.add_rmsnorm_quant(x, r, w, EPS)
+    assert np.all(_bits_to_f64(h) == 0) and np.all(y == 0)
+    assert np.all(sl == 0) and np.all((q & 0x7F) == 0)
