@@ -314,6 +314,17 @@ def sweep(args, mx, synth, torch, dev):
     gbs = norm_bytes(NORM_ROWS, N_MODEL) / med / 1e9
     print(json.dumps({"kind": "rmsnorm_quant", "rows": NORM_ROWS, "hidden": N_MODEL, "us_median": round(med * 1e6, 2),
                       "GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}), flush=True)
+    # residual add + norm quantiser (the decode fusion without its all-reduce)
+    for rows in (128, NORM_ROWS):
+        xr, wr = synth.norm_inputs_bf16(rows, N_MODEL)
+        xr, wr = xr.to(dev), wr.to(dev)
+        res = synth.normal_bf16((rows, N_MODEL), sigma=2.0, seed=9).to(dev)
+        med, p10, p90 = timed(lambda: mx.add_rmsnorm_quant(xr, res, wr, 1e-6), max(args.steps, 10))
+        nbytes = norm_bytes(rows, N_MODEL) + 4 * rows * N_MODEL  # + residual read and write
+        gbs = nbytes / med / 1e9
+        print(json.dumps({"kind": "add_rmsnorm_quant", "rows": rows, "hidden": N_MODEL,
+                          "us_median": round(med * 1e6, 2), "GB/s": round(gbs, 1),
+                          "frac_hbm": round(gbs / PEAK_HBM_GBS, 4)}), flush=True)
     # fused dense GEMM1: gate_up [2 * 3072, 6144] GEMM + SiLU(gate) * up + MXFP8 quantisation
     inter, hidden = K_DOWN, N_MODEL
     wq_gu, _, ws_gu = mx.quantize(synth.weights_bf16(2 * inter, hidden, seed=1).to(dev), linear=False)

@@ -1,10 +1,11 @@
 /*
  * mxfp8.h - C ABI of the MI355X (gfx950) MXFP8 library.
  *
- * Five operations, each one or two HIP kernels, all asynchronous on the
+ * Six operations, each one or two HIP kernels, all asynchronous on the
  * caller's stream:
  *   mxfp8_quantize        BF16 [rows,k] -> E4M3 [rows,k] + UE8M0 scales (one per 32 along k)
  *   rmsnorm_quant_mxfp8   Gemma RMSNorm fused with the same quantisation
+ *   add_rmsnorm_quant_mxfp8  the same after a residual add (residual stream updated in place)
  *   mxfp8_swizzle_scales  linear scales -> 128x4 swizzled scales (after a gather)
  *   mxfp8_gemm_bf16out    C[m,n] = sum_k A[m,k] B[n,k] with per-32-K block scales, BF16 out,
  *                         written in M-row chunks (one chunk = one rank's reduce-scatter shard)
@@ -113,6 +114,29 @@ int rmsnorm_quant_mxfp8(const void* x_bf16, const void* w_bf16, int64_t rows, in
 int rmsnorm_quant_mxfp8_check(const void* x_bf16, const void* w_bf16, int64_t rows, int64_t hidden,
                               int64_t ldx, const void* q_e4m3, const void* scales_linear,
                               const void* scales_swizzled);
+
+/*
+ * add_rmsnorm_quant_mxfp8 - the residual add in front of the Gemma RMSNorm quantiser: the
+ * decode fusion of PR #64111 ("Claims": all-reduce + Gemma norm + MXFP8 quant) without the
+ * all-reduce, whose output is x here.
+ *   h = BF16(x + residual)   (exact sum rounded once to nearest even), written back to residual;
+ *   then exactly rmsnorm_quant_mxfp8 applied to h.
+ *
+ *   x_bf16          [rows, hidden] BF16, row stride ldx (as for rmsnorm_quant_mxfp8).
+ *   residual_bf16   [rows, hidden] BF16, row stride ldr (ldr >= hidden, ldr % 8 == 0), 16-byte
+ *                   aligned; read and overwritten with h. Must not overlap x.
+ *   w_bf16, eps, q_e4m3, scales_linear, scales_swizzled, hidden limits: as for rmsnorm_quant_mxfp8.
+ *   rows == 0 is a no-op (pointers may be NULL).
+ */
+int add_rmsnorm_quant_mxfp8(const void* x_bf16, void* residual_bf16, const void* w_bf16, int64_t rows,
+                            int64_t hidden, int64_t ldx, int64_t ldr, float eps, void* q_e4m3,
+                            void* scales_linear, void* scales_swizzled, hipStream_t stream);
+
+/* Host-side argument check of add_rmsnorm_quant_mxfp8 (same rules, no HIP call). */
+int add_rmsnorm_quant_mxfp8_check(const void* x_bf16, const void* residual_bf16, const void* w_bf16,
+                                  int64_t rows, int64_t hidden, int64_t ldx, int64_t ldr,
+                                  const void* q_e4m3, const void* scales_linear,
+                                  const void* scales_swizzled);
 
 /*
  * mxfp8_swizzle_scales - linear UE8M0 scales -> the 128x4 swizzled layout, the step after an

@@ -55,6 +55,10 @@ def load_library():
     lib.rmsnorm_quant_mxfp8.argtypes = [vp, vp, i64, i64, i64, f32, vp, vp, vp, vp]
     lib.rmsnorm_quant_mxfp8_check.restype = i32
     lib.rmsnorm_quant_mxfp8_check.argtypes = [vp, vp, i64, i64, i64, vp, vp, vp]
+    lib.add_rmsnorm_quant_mxfp8.restype = i32
+    lib.add_rmsnorm_quant_mxfp8.argtypes = [vp, vp, vp, i64, i64, i64, i64, f32, vp, vp, vp, vp]
+    lib.add_rmsnorm_quant_mxfp8_check.restype = i32
+    lib.add_rmsnorm_quant_mxfp8_check.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, vp, vp]
     lib.mxfp8_swizzle_scales.restype = i32
     lib.mxfp8_swizzle_scales.argtypes = [vp, i64, i64, vp, vp]
     lib.mxfp8_swizzle_scales_check.restype = i32
@@ -152,6 +156,33 @@ def rmsnorm_quant(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, linear: b
                                             _ptr(s_lin), _ptr(s_swz), _stream(x))
     if st != OK:
         raise MXFP8Error("rmsnorm_quant_mxfp8", st)
+    return q, s_lin, s_swz
+
+
+def add_rmsnorm_quant(x: torch.Tensor, residual: torch.Tensor, w: torch.Tensor, eps: float = 1e-6,
+                      linear: bool = True, swizzled: bool = True, out=None):
+    """Residual add then Gemma RMSNorm quantised to MXFP8: ``residual <- BF16(x + residual)`` (in
+    place), then the norm quantiser of the updated residual. Returns ``(q, scales_linear,
+    scales_swizzled)``."""
+    _rows_view(x, "x", torch.bfloat16)
+    _rows_view(residual, "residual", torch.bfloat16)
+    _dev(w, "w")
+    rows, h = x.shape
+    if residual.shape != x.shape:
+        raise ValueError("residual must have the shape of x")
+    if w.dtype != torch.bfloat16 or w.shape != (h,) or not w.is_contiguous():
+        raise ValueError("w must be a contiguous bfloat16 [hidden] tensor")
+    if out is not None:
+        q, s_lin, s_swz = out
+    else:
+        q = torch.empty((rows, h), dtype=torch.uint8, device=x.device)
+        s_lin = torch.empty((rows, h // 32), dtype=torch.uint8, device=x.device) if linear else None
+        s_swz = torch.empty(scale_bytes(rows, h, SWIZZLED), dtype=torch.uint8, device=x.device) if swizzled else None
+    st = load_library().add_rmsnorm_quant_mxfp8(_ptr(x), _ptr(residual), _ptr(w), rows, h, x.stride(0),
+                                                residual.stride(0), float(eps), _ptr(q), _ptr(s_lin), _ptr(s_swz),
+                                                _stream(x))
+    if st != OK:
+        raise MXFP8Error("add_rmsnorm_quant_mxfp8", st)
     return q, s_lin, s_swz
 
 

@@ -74,7 +74,35 @@ int rmsnorm_quant_mxfp8(const void* x_bf16, const void* w_bf16, int64_t rows, in
   if (st != MXFP8_OK) return st;
   return hip_status(mxfp8::launch_rmsnorm_quant((const uint16_t*)x_bf16, (const uint16_t*)w_bf16, rows,
                                                 hidden, ldx, eps, (uint8_t*)q_e4m3,
-                                                (uint8_t*)scales_linear, (uint8_t*)scales_swizzled, stream));
+                                                (uint8_t*)scales_linear, (uint8_t*)scales_swizzled, nullptr,
+                                                0, stream));
+}
+
+int add_rmsnorm_quant_mxfp8_check(const void* x_bf16, const void* residual_bf16, const void* w_bf16,
+                                  int64_t rows, int64_t hidden, int64_t ldx, int64_t ldr, const void* q_e4m3,
+                                  const void* scales_linear, const void* scales_swizzled) {
+  const int st = rmsnorm_quant_mxfp8_check(x_bf16, w_bf16, rows, hidden, ldx, q_e4m3, scales_linear,
+                                           scales_swizzled);
+  if (st != MXFP8_OK || rows == 0) return st;
+  if (!residual_bf16 || ldr < hidden) return MXFP8_EINVAL;
+  if (!aligned(residual_bf16, 16) || ldr % 8 != 0) return MXFP8_EALIGN;
+  // x and the residual stream must not overlap (each row of the residual is rewritten)
+  const uintptr_t x0 = (uintptr_t)x_bf16, x1 = x0 + (uintptr_t)(((rows - 1) * ldx + hidden) * 2);
+  const uintptr_t r0 = (uintptr_t)residual_bf16, r1 = r0 + (uintptr_t)(((rows - 1) * ldr + hidden) * 2);
+  if (x0 < r1 && r0 < x1) return MXFP8_EINVAL;
+  return MXFP8_OK;
+}
+
+int add_rmsnorm_quant_mxfp8(const void* x_bf16, void* residual_bf16, const void* w_bf16, int64_t rows,
+                            int64_t hidden, int64_t ldx, int64_t ldr, float eps, void* q_e4m3,
+                            void* scales_linear, void* scales_swizzled, hipStream_t stream) {
+  const int st = add_rmsnorm_quant_mxfp8_check(x_bf16, residual_bf16, w_bf16, rows, hidden, ldx, ldr, q_e4m3,
+                                               scales_linear, scales_swizzled);
+  if (st != MXFP8_OK) return st;
+  return hip_status(mxfp8::launch_rmsnorm_quant((const uint16_t*)x_bf16, (const uint16_t*)w_bf16, rows,
+                                                hidden, ldx, eps, (uint8_t*)q_e4m3,
+                                                (uint8_t*)scales_linear, (uint8_t*)scales_swizzled,
+                                                (uint16_t*)residual_bf16, ldr, stream));
 }
 
 int mxfp8_swizzle_scales_check(const void* scales_linear, int64_t rows, int64_t k,

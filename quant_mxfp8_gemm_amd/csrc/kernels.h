@@ -10,9 +10,11 @@ namespace mxfp8 {
 hipError_t launch_quantize(const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, uint8_t* q,
                            uint8_t* s_lin, uint8_t* s_swz, hipStream_t stream);
 
+// res: null, or the residual stream [rows, hidden] (row stride ldr) that x is first added to;
+// it is overwritten with BF16(x + res) and the norm is taken of that sum.
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* w, int64_t rows, int64_t hidden,
                                 int64_t ldx, float eps, uint8_t* q, uint8_t* s_lin, uint8_t* s_swz,
-                                hipStream_t stream);
+                                uint16_t* res, int64_t ldr, hipStream_t stream);
 
 // Zero the pad bytes of a swizzled scale buffer for a [rows, k] operand (no-op without padding).
 hipError_t launch_swizzle_pad_zero(uint8_t* s_swz, int64_t rows, int64_t k, hipStream_t stream);

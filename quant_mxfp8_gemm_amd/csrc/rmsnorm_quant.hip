@@ -24,13 +24,23 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-template <int CPT, bool LIN, bool SWZ>
+// Two BF16 pairs added and rounded back to BF16 (nearest even). The fp32 sum of two BF16
+// values rounded to BF16 equals their exact sum rounded once: fp32 carries more than twice
+// BF16's precision plus two bits, so the intermediate rounding cannot move the result.
+__device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b) {
+  return f32_to_bf16_rne(bf16_lo(a) + bf16_lo(b)) | (f32_to_bf16_rne(bf16_hi(a) + bf16_hi(b)) << 16);
+}
+
+// RES: the row is first replaced by h = BF16(x + res) (written back to res, the residual
+// stream) and the norm is taken of h.
+template <int CPT, bool LIN, bool SWZ, bool RES>
 __global__ __launch_bounds__(RT) void rmsnorm_quant_kernel(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ w, int hidden,
                                                            int64_t ldx, double eps,
                                                            uint8_t* __restrict__ q,
                                                            uint8_t* __restrict__ s_lin,
-                                                           uint8_t* __restrict__ s_swz) {
+                                                           uint8_t* __restrict__ s_swz,
+                                                           uint16_t* __restrict__ res, int64_t ldr) {
   __shared__ double partial[RT / 64];
   const int64_t row = blockIdx.x;
   const int cpr = hidden >> 3;
@@ -50,6 +60,13 @@ __global__ __launch_bounds__(RT) void rmsnorm_quant_kernel(const uint16_t* __res
     const int c8 = u * RT + (int)threadIdx.x;
     if (c8 < cpr) {
       v[u] = *(const uint4*)(xr + c8 * 8);
+      if (RES) {
+        uint16_t* rp = res + row * ldr + c8 * 8;
+        const uint4 rv = *(const uint4*)rp;
+        v[u] = make_uint4(add_bf16x2(v[u].x, rv.x), add_bf16x2(v[u].y, rv.y), add_bf16x2(v[u].z, rv.z),
+                          add_bf16x2(v[u].w, rv.w));
+        *(uint4*)rp = v[u];
+      }
       const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -107,38 +124,45 @@ __global__ __launch_bounds__(RT) void rmsnorm_quant_kernel(const uint16_t* __res
   }
 }
 
-template <int CPT>
-hipError_t launch_cpt(const uint16_t* x, const uint16_t* w, int64_t rows, int hidden, int64_t ldx, double eps,
-                      uint8_t* q, uint8_t* s_lin, uint8_t* s_swz, hipStream_t stream) {
+template <int CPT, bool RES>
+hipError_t launch_res(const uint16_t* x, const uint16_t* w, int64_t rows, int hidden, int64_t ldx, double eps,
+                      uint8_t* q, uint8_t* s_lin, uint8_t* s_swz, uint16_t* res, int64_t ldr, hipStream_t stream) {
   const dim3 grid((unsigned)rows), block(RT);
   if (s_lin && s_swz)
-    rmsnorm_quant_kernel<CPT, true, true><<<grid, block, 0, stream>>>(x, w, hidden, ldx, eps, q, s_lin, s_swz);
+    rmsnorm_quant_kernel<CPT, true, true, RES><<<grid, block, 0, stream>>>(x, w, hidden, ldx, eps, q, s_lin, s_swz, res, ldr);
   else if (s_lin)
-    rmsnorm_quant_kernel<CPT, true, false><<<grid, block, 0, stream>>>(x, w, hidden, ldx, eps, q, s_lin, s_swz);
+    rmsnorm_quant_kernel<CPT, true, false, RES><<<grid, block, 0, stream>>>(x, w, hidden, ldx, eps, q, s_lin, s_swz, res, ldr);
   else
-    rmsnorm_quant_kernel<CPT, false, true><<<grid, block, 0, stream>>>(x, w, hidden, ldx, eps, q, s_lin, s_swz);
+    rmsnorm_quant_kernel<CPT, false, true, RES><<<grid, block, 0, stream>>>(x, w, hidden, ldx, eps, q, s_lin, s_swz, res, ldr);
   return hipGetLastError();
+}
+
+template <int CPT>
+hipError_t launch_cpt(const uint16_t* x, const uint16_t* w, int64_t rows, int hidden, int64_t ldx, double eps,
+                      uint8_t* q, uint8_t* s_lin, uint8_t* s_swz, uint16_t* res, int64_t ldr, hipStream_t stream) {
+  if (res) return launch_res<CPT, true>(x, w, rows, hidden, ldx, eps, q, s_lin, s_swz, res, ldr, stream);
+  return launch_res<CPT, false>(x, w, rows, hidden, ldx, eps, q, s_lin, s_swz, nullptr, 0, stream);
 }
 
 }  // namespace
 
 hipError_t launch_rmsnorm_quant(const uint16_t* x, const uint16_t* w, int64_t rows, int64_t hidden,
                                 int64_t ldx, float eps, uint8_t* q, uint8_t* s_lin, uint8_t* s_swz,
-                                hipStream_t stream) {
+                                uint16_t* res, int64_t ldr, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const int cpt = (int)((hidden / 8 + RT - 1) / RT);  // 1..8 (hidden <= 16384)
   const double e = (double)eps;
   const int h = (int)hidden;
   hipError_t err;
   switch (cpt) {
-    case 1: err = launch_cpt<1>(x, w, rows, h, ldx, e, q, s_lin, s_swz, stream); break;
-    case 2: err = launch_cpt<2>(x, w, rows, h, ldx, e, q, s_lin, s_swz, stream); break;
-    case 3: err = launch_cpt<3>(x, w, rows, h, ldx, e, q, s_lin, s_swz, stream); break;
-    case 4: err = launch_cpt<4>(x, w, rows, h, ldx, e, q, s_lin, s_swz, stream); break;
-    case 5: err = launch_cpt<5>(x, w, rows, h, ldx, e, q, s_lin, s_swz, stream); break;
-    case 6: err = launch_cpt<6>(x, w, rows, h, ldx, e, q, s_lin, s_swz, stream); break;
-    case 7: err = launch_cpt<7>(x, w, rows, h, ldx, e, q, s_lin, s_swz, stream); break;
-    default: err = launch_cpt<8>(x, w, rows, h, ldx, e, q, s_lin, s_swz, stream); break;
+    case 1: err = launch_cpt<1>(x, w, rows, h, ldx, e, q, s_lin, s_swz, res, ldr, stream); break;
+    case 2: err = launch_cpt<2>(x, w, rows, h, ldx, e, q, s_lin, s_swz, res, ldr, stream); break;
+    case 3: err = launch_cpt<3>(x, w, rows, h, ldx, e, q, s_lin, s_swz, res, ldr, stream); break;
+    case 4: err = launch_cpt<4>(x, w, rows, h, ldx, e, q, s_lin, s_swz, res, ldr, stream); break;
+    case 5: err = launch_cpt<5>(x, w, rows, h, ldx, e, q, s_lin, s_swz, res, ldr, stream); break;
+    case 6: err = launch_cpt<6>(x, w, rows, h, ldx, e, q, s_lin, s_swz, res, ldr, stream); break;
+    case 7: err = launch_cpt<7>(x, w, rows, h, ldx, e, q, s_lin, s_swz, res, ldr, stream); break;
+    default: err = launch_cpt<8>(x, w, rows, h, ldx, e, q, s_lin, s_swz, res, ldr, stream); break;
   }
   if (err != hipSuccess) return err;
   if (s_swz) err = launch_swizzle_pad_zero(s_swz, rows, hidden, stream);

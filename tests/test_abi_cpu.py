@@ -35,7 +35,8 @@ def lib():
 def test_header_declares_the_three_operations():
     names = _declared_functions()
     for f in ("mxfp8_quantize", "rmsnorm_quant_mxfp8", "mxfp8_gemm_bf16out", "mxfp8_swizzle_scales",
-              "mxfp8_gemm_silu_mul_quant", "mxfp8_scale_bytes", "mxfp8_status_string"):
+              "mxfp8_gemm_silu_mul_quant", "add_rmsnorm_quant_mxfp8", "mxfp8_scale_bytes",
+              "mxfp8_status_string"):
         assert f in names
 
 
@@ -87,6 +88,19 @@ def test_rmsnorm_check(lib):
     assert c(P, P, 1024, 6150, 6150, P, P, P) == EINVAL
     assert c(P, P, 1024, 32768, 32768, P, P, P) == EUNSUP
     assert c(P, P + 2, 1024, 6144, 6144, P, P, P) == EALIGN
+
+
+def test_add_rmsnorm_check(lib):
+    c = lib.add_rmsnorm_quant_mxfp8_check
+    R = P + (64 << 20)   # a residual buffer well clear of x
+    assert c(P, R, P, 1024, 6144, 6144, 6144, P, P, P) == OK
+    assert c(None, None, None, 0, 6144, 6144, 6144, None, None, None) == OK
+    assert c(P, None, P, 1024, 6144, 6144, 6144, P, P, P) == EINVAL     # no residual
+    assert c(P, R, P, 1024, 6144, 6144, 6000, P, P, P) == EINVAL        # ldr < hidden
+    assert c(P, R + 8, P, 1024, 6144, 6144, 6144, P, P, P) == EALIGN    # residual alignment
+    assert c(P, R, P, 1024, 6144, 6144, 6148, P, P, P) == EALIGN        # ldr % 8
+    assert c(P, P + 4096, P, 1024, 6144, 6144, 6144, P, P, P) == EINVAL  # overlaps x
+    assert c(P, R, P, 1024, 6150, 6150, 6150, P, P, P) == EINVAL        # hidden % 32
 
 
 def test_swizzle_check(lib):

@@ -105,3 +105,25 @@ def test_rmsnorm_weight_minus_one_gives_zero_codes():
 def test_rmsnorm_single_layout(linear, swizzled):
     x, w = synth.norm_inputs_bf16(64, 512)
     _check(x, w, linear=linear, swizzled=swizzled)
+
+
+@pytest.mark.parametrize("rows,h", [(1024, 6144), (37, 4096), (5, 96)])
+def test_add_rmsnorm_matches_oracle(rows, h):
+    """Residual add + norm quantiser: the updated residual is bit-exact and the codes and scales
+    meet the same bar as the plain norm quantiser."""
+    print(f"add_rmsnorm rows={rows} hidden={h}", flush=True)
+    x, w = synth.norm_inputs_bf16(rows, h)
+    r = synth.normal_bf16((rows, h), seed=9, sigma=2.0)
+    q_ref, sl_ref, ss_ref, h_ref, y_ref = oracle.add_rmsnorm_quant(bits16(x), bits16(r), bits16(w), EPS)
+    rd = r.cuda().clone()
+    q, sl, ss = mx.add_rmsnorm_quant(x.cuda(), rd, w.cuda(), EPS)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits16(rd), h_ref), "residual stream"
+    near = _near_boundary(y_ref)
+    sdiff = np.abs(sl.cpu().numpy().astype(int) - sl_ref.astype(int))
+    assert np.all(sdiff[~near] == 0) and np.all(sdiff <= 1)
+    steps = e4m3_step_diff(q.cpu().numpy(), q_ref)
+    if int(sdiff.sum()) == 0:
+        assert np.array_equal(ss.cpu().numpy(), ss_ref)
+        assert np.all(steps <= 1)
+    print(f"  scale diffs {int((sdiff != 0).sum())}, code diffs {int((steps != 0).sum())}", flush=True)
