@@ -162,6 +162,29 @@ def test_gemm_o_proj_m32768():
     _sampled(32768, 2048, mx.SWIZZLED, "act")
 
 
+@pytest.mark.parametrize("m,n,k,chunks", [(64, 1, 128, 1), (33, 17, 256, 1), (200, 40, 16384, 2),
+                                          (4, 300, 640, 4), (130, 3, 1152, 2)])
+def test_gemm_edge_shapes_full(m, n, k, chunks):
+    """Degenerate widths (N = 1, 3, 17), a long K (16384), M below one tile, odd K steps."""
+    print(f"gemm edge m={m} n={n} k={k} chunks={chunks}", flush=True)
+    qa, sa, qb, sb = _operands(m, n, k, seed_a=m + 7, seed_b=n + 7)
+    ref = oracle.gemm(qa, sa[1], 1, qb, sb[0], 0)
+    c = _gpu_gemm(qa, sa[1], 1, qb, sb[0], 0, num_chunks=chunks)
+    _assert_close(c, ref, _abs_sum_full(qa, sa[1], 1, qb, sb[0], 0), f"edge m={m} n={n} k={k}")
+
+
+def test_gemm_chunk_counters_small_tiles():
+    """chunk_done with the smallest tiles (32 rows per chunk): every chunk counts all its tiles
+    and the output does not depend on the chunking."""
+    m, n, k = 128, 6144, 512
+    qa, sa, qb, sb = _operands(m, n, k)
+    c1 = _gpu_gemm(qa, sa[0], 0, qb, sb[0], 0, num_chunks=1)
+    done = torch.zeros(4, dtype=torch.int32, device="cuda")
+    c4 = _gpu_gemm(qa, sa[0], 0, qb, sb[0], 0, num_chunks=4, first_chunk=3, chunk_done=done)
+    assert np.array_equal(c1, c4)
+    assert done.cpu().tolist() == [mx.gemm_tiles_per_chunk(m, n, 4)] * 4 == [48] * 4
+
+
 def test_gemm_chunking_is_bitwise_invariant():
     m, n, k = 1536, N_MODEL, 512
     qa, sa, qb, sb = _operands(m, n, k)

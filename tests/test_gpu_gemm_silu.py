@@ -72,6 +72,17 @@ def test_gemm_silu_mul_quant_full(m, inter, k, tile_m, la, lw):
     assert np.mean(q == q_ref) > 0.99 and np.mean(s_lin == s_ref) > 0.99
 
 
+@pytest.mark.parametrize("m,inter,k", [(1, 32, 128), (3, 96, 384)])
+def test_gemm_silu_mul_quant_minimal(m, inter, k):
+    """The smallest shapes: one row, one 32-block of the intermediate dimension."""
+    qa, sa, qw, sw = _operands(m, inter, k, seed_a=5, seed_w=6)
+    q, s_lin, s_swz = _run(qa, sa[0], 0, qw, sw[0], 0)
+    q_ref, s_ref, _, gu = oracle.gemm_silu_mul_quant(qa, sa[0], 0, qw, sw[0], 0, want_gu=True)
+    mass = _mass(qa, sa[0], 0, qw, sw[0], 0, range(m))
+    silu_mul_quant_check(q, s_lin, gu, mass, inter)
+    assert np.array_equal(s_swz, oracle.swizzle_scales(s_lin))
+
+
 def test_gemm_silu_mul_quant_workload_rows():
     """M = 32768, inter = 3072, K = 6144 (the dense MLP per TP4 rank feeding down_proj K = 3072)."""
     m, inter, k = 32768, 3072, 6144
