@@ -29,8 +29,9 @@
  *                                by rows, so the quantisers can emit both layouts in one pass.
  *
  * Ownership and threading: the caller owns every buffer (device memory unless
- * stated). The library allocates nothing, keeps no state between calls and is
- * safe to call from several host threads. Every call validates its arguments on
+ * stated). The library allocates nothing, keeps no state between calls beyond a
+ * per-device cache of the compute-unit count, and is safe to call from several
+ * host threads. Every call validates its arguments on
  * the host first and returns a negative status without touching the GPU if they
  * are invalid; on success the work is enqueued on `stream` (0 = null stream) and
  * MXFP8_OK is returned. A failed launch returns MXFP8_EHIP. The library never
