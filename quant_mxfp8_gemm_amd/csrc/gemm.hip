@@ -419,6 +419,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
 // Tile configurations: output tile, wave grid, LDS stages.
 using TileL = Tile<256, 256, 4, 2, 2>;  // 8 waves of 64 x 128; large problems
 using TileN = Tile<256, 192, 4, 2, 2>;  // 8 waves of 64 x 96; when 256 x 256 leaves a round part-empty
+using TileW = Tile<128, 192, 4, 2, 3>;  // 8 waves of 32 x 96
 using TileM = Tile<128, 128, 4, 2, 4>;  // 8 waves of 32 x 64
 using TileS = Tile<64, 128, 2, 4, 4>;   // 8 waves of 32 x 32
 using TileT = Tile<32, 128, 1, 4, 4>;   // 4 waves of 32 x 32; a few rows per chunk
@@ -441,28 +442,39 @@ int64_t tile_count(int64_t m, int64_t n, int num_chunks, int bm, int bn) {
   return (int64_t)num_chunks * ((m / num_chunks + bm - 1) / bm) * ((n + bn - 1) / bn);
 }
 
-enum { CFG_L, CFG_N, CFG_M, CFG_S, CFG_T };
+enum { CFG_L, CFG_N, CFG_W, CFG_M, CFG_S, CFG_T };
 
-// Tile choice. Between the two 256-row tiles the one with the shorter estimated makespan wins:
-// rounds of workgroups over the compute units times the work of one tile, the narrower tile
-// charged 5% for its lower data reuse (it wins when 256 x 256 tiles leave the last round
-// part-empty). Otherwise the largest tile that fits a chunk's rows and still gives about three
-// quarters of the compute units a tile: the smaller ones trade reuse per LDS byte for more
-// workgroups and more stages in flight.
+// Tile choice by estimated makespan: rounds of workgroups over the compute units times the
+// time of one tile. A tile's K step costs its MFMA work (BM x BN; 256 x 192 charged 5% for
+// its lower reuse per loaded byte) but no less than a latency floor measured at about the
+// work of a 256 x 256 step / 2.25: below that a workgroup waits on its loads and barriers,
+// not on the MFMAs. Among equal estimates the configuration with more tiles wins (more
+// workgroups in flight). A tile must fit in a chunk's rows.
+struct CfgInfo {
+  int id, bm, bn;
+  double charge;
+};
+constexpr CfgInfo kCfgs[] = {{CFG_L, 256, 256, 1.0},  {CFG_N, 256, 192, 1.05}, {CFG_W, 128, 192, 1.0},
+                             {CFG_M, 128, 128, 1.0},  {CFG_S, 64, 128, 1.0},   {CFG_T, 32, 128, 1.0}};
+constexpr double kStepFloor = 256.0 * 256.0 / 2.25;
+
 int pick_config(int64_t m, int64_t n, int num_chunks) {
   const int64_t rows = m / num_chunks;
-  const int64_t want = 3 * REF_CUS / 4;
-  if (rows >= TileL::BM) {
-    const int64_t tl = tile_count(m, n, num_chunks, TileL::BM, TileL::BN);
-    const int64_t tn = tile_count(m, n, num_chunks, TileN::BM, TileN::BN);
-    const double span_l = (double)((tl + REF_CUS - 1) / REF_CUS) * TileL::BM * TileL::BN;
-    const double span_n = (double)((tn + REF_CUS - 1) / REF_CUS) * TileN::BM * TileN::BN * 1.05;
-    if (span_n < span_l && tn >= want) return CFG_N;
-    if (tl >= want) return CFG_L;
+  int best = CFG_T;
+  double best_span = 0.0;
+  int64_t best_tiles = 0;
+  for (const CfgInfo& c : kCfgs) {
+    if (c.id != CFG_T && rows < c.bm) continue;  // the 32-row tile takes any chunk
+    const int64_t tiles = tile_count(m, n, num_chunks, c.bm, c.bn);
+    const double step = (double)c.bm * c.bn * c.charge;
+    const double span = (double)((tiles + REF_CUS - 1) / REF_CUS) * (step > kStepFloor ? step : kStepFloor);
+    if (best_tiles == 0 || span < best_span * 0.999 || (span <= best_span * 1.001 && tiles > best_tiles)) {
+      best = c.id;
+      best_span = span;
+      best_tiles = tiles;
+    }
   }
-  if (rows >= TileM::BM && tile_count(m, n, num_chunks, TileM::BM, TileM::BN) >= want) return CFG_M;
-  if (rows >= TileS::BM && tile_count(m, n, num_chunks, TileS::BM, TileS::BN) >= want) return CFG_S;
-  return CFG_T;
+  return best;
 }
 
 template <class T, int EPI = EPI_BF16>
@@ -491,6 +503,7 @@ GemmShape gemm_pick_shape(int64_t m, int64_t n, int num_chunks) {
   switch (pick_config(m, n, num_chunks)) {
     case CFG_L: return GemmShape{TileL::BM, TileL::BN};
     case CFG_N: return GemmShape{TileN::BM, TileN::BN};
+    case CFG_W: return GemmShape{TileW::BM, TileW::BN};
     case CFG_M: return GemmShape{TileM::BM, TileM::BN};
     case CFG_S: return GemmShape{TileS::BM, TileS::BN};
     default: return GemmShape{TileT::BM, TileT::BN};
@@ -506,6 +519,7 @@ hipError_t launch_gemm_silu_mul_quant(const uint8_t* a, const uint8_t* as, int a
   switch (pick_config(m, n, 1)) {
     case CFG_L: e = launch_cfg<TileL, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
     case CFG_N: e = launch_cfg<TileN, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
+    case CFG_W: e = launch_cfg<TileW, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
     case CFG_M: e = launch_cfg<TileM, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
     case CFG_S: e = launch_cfg<TileS, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
     default: e = launch_cfg<TileT, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
@@ -523,6 +537,8 @@ hipError_t launch_gemm(const uint8_t* a, const uint8_t* as, int a_layout, const 
       return launch_cfg<TileL>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
     case CFG_N:
       return launch_cfg<TileN>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
+    case CFG_W:
+      return launch_cfg<TileW>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
     case CFG_M:
       return launch_cfg<TileM>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
     case CFG_S:

@@ -174,7 +174,8 @@ def test_tiles_per_chunk(lib):
     assert lib.mxfp8_gemm_tiles_per_chunk(10, 10, 3) == -1
     # the tile shrinks when a 256 x 256 tiling leaves the compute units idle
     assert mx.gemm_tiles_per_chunk(32768, 6144, 4) == 32 * 24    # 256 x 256
-    assert mx.gemm_tiles_per_chunk(1024, 6144, 4) == 2 * 48      # 128 x 128
+    assert mx.gemm_tiles_per_chunk(1024, 6144, 4) == 2 * 32      # 128 x 192: one full round
+    assert mx.gemm_tiles_per_chunk(512, 6144, 4) == 1 * 48       # 128 x 128
     assert mx.gemm_tiles_per_chunk(4096, 6144, 4) == 4 * 32      # 256 x 192: two full rounds
     assert mx.gemm_tiles_per_chunk(256, 6144, 1) == 4 * 48       # 64 x 128
     assert mx.gemm_tiles_per_chunk(128, 6144, 1) == 4 * 48       # 32 x 128
