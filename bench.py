@@ -53,8 +53,8 @@ def _parse():
 # counter of a 1 GiB copy onto 1 GiB. Valid only for the kernel code it was taken on
 # (gemm_code_sha256).
 GEMM_TRAFFIC = {
-    "source_sha256": "07b5efab8890ed455a28f321eb8c6fa8bba6d50e55b0ea28ee128915233d0b3a",
-    "fetch_kib": 456265.1, "write_kib": 393595.3,
+    "source_sha256": "417879571280298f9057b3cc9e0550bf91c684c8e7eab37d953c789dfa8ab898",
+    "fetch_kib": 456272.2, "write_kib": 393497.4,
     "fetch_factor": 2.0, "write_factor": 1.0,
 }
 
