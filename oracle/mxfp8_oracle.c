@@ -1,5 +1,7 @@
 /*
- * mxfp8_oracle.c - plain CPU definition of the three MXFP8 operations.
+ * mxfp8_oracle.c - plain CPU definition of the MXFP8 operations: the quantiser, the
+ * Gemma RMSNorm quantiser (with and without a residual add), the block-scaled GEMM, the
+ * fused dense GEMM1 (gate_up GEMM, SiLU(gate) * up, quantiser) and the scale swizzle.
  *
  * TEST INFRASTRUCTURE ONLY. This file is the correctness oracle of the HIP
  * library: it is loaded by the test suite, by the smoke check and by the CPU
@@ -36,14 +38,25 @@
  *    2^(sa[m,kb]-127) * 2^(sb[n,kb]-127) * sum_{i<32} A[m,32kb+i] * B[n,32kb+i],
  *    rounded once to BF16 (round to nearest even). A is [M,K] and B is [N,K],
  *    both K-contiguous.
+ *  - The fused dense GEMM1 (PR #65496 "Details", PR #64111 "Claims"): with the
+ *    merged gate_up weight (gate rows, then up rows), y = SiLU(g) * u where
+ *    SiLU(g) = g / (1 + e^-g), g and u exact GEMM values, y in fp64 rounded once
+ *    to fp32 and quantised like the norm output.
+ *  - The residual add ahead of the norm: h = BF16(x + r), one rounding of the
+ *    exact sum; the norm is taken of h.
  *
  * Inexact steps: only the outer fp64 sum over K-blocks of the GEMM and the
  * fp64 RMSNorm arithmetic round. Each 32-term block product sum is exact in
  * fp64 (8-bit significand products spanning < 2^42 fit in 53 bits).
  *
- * Precision of decisions: the HIP norm computes y in fp32 before quantising
- * it, so this oracle rounds its fp64 y once to fp32 and takes the scale and
- * code decisions on that fp32 value, exactly (in fp64 arithmetic).
+ * Precision of decisions: the HIP norm and the fused GEMM1 quantise an fp32 y,
+ * so this oracle rounds its fp64 y once to fp32 and takes the scale and code
+ * decisions on that fp32 value, exactly (in fp64 arithmetic).
+ *
+ * Every function is pinned by the CPU tests (tests/test_oracle_pins.py) against
+ * values fixed outside this file: golden values, torch's E4M3 and BF16 casts and
+ * SiLU, closed forms, brute force on small inputs and an independent
+ * reshape/transpose construction of the swizzle.
  *
  * Inputs are BF16 bit patterns (uint16). Non-finite inputs are outside the
  * contract; the quantisers report them with a negative return value.
