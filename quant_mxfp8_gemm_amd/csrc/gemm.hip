@@ -47,14 +47,18 @@ namespace {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BK = 128;  // K bytes per stage
 constexpr int GM = 4;    // tile-rows per group
 
-template <int BM_, int BN_, int WMW, int WNW, int NS_>
+template <int BM_, int BN_, int WMW, int WNW, int NS_, bool SPLIT_ = false>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, NS = NS_;
+  // SPLIT: A in a ring of two stage buffers and B in a ring of three (B is fetched two steps
+  // ahead), the scales in registers; NS is not used
+  static constexpr bool SPLIT = SPLIT_;
   static constexpr int NW = WMW * WNW, NT = NW * 64;
   static constexpr int WTM = BM / WMW, WTN = BN / WNW;  // wave sub-tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;    // MFMA blocks per wave
@@ -66,7 +70,8 @@ struct Tile {
   static constexpr int DS = (SROWS + 63) / 64;    // scale loads per wave per stage
   static constexpr int LOADS = DA + DB + DS;      // LDS-DMA instructions per wave per stage
   static constexpr int C_STRIDE = BN * 2 + 16;    // bytes per staged output row
-  static constexpr int LDS_BYTES = NS * STAGE > BM * C_STRIDE ? NS * STAGE : BM * C_STRIDE;
+  static constexpr int RING_BYTES = SPLIT ? 2 * A_BYTES + 3 * B_BYTES : NS * STAGE;
+  static constexpr int LDS_BYTES = RING_BYTES > BM * C_STRIDE ? RING_BYTES : BM * C_STRIDE;
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(DA * NW * 1024 == A_BYTES && DB * NW * 1024 == B_BYTES, "data split");
   static_assert(SROWS * NW == BM + BN && (SROWS % 64 == 0 || SROWS < 64), "scale split");
@@ -104,6 +109,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 template <int SEL>
 __device__ __forceinline__ v16f mfma(const v8i& a, const v8i& b, const v16f& c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, SEL, sa, SEL, sb);
+}
+
+// Wait as wait_vm<N>, and tell the compiler that the two scale vectors are only final after
+// it: they are the destinations of loads the compiler does not track (split ring below).
+template <int N>
+__device__ __forceinline__ void wait_vm_regs(u32x2& a, u32x4& b) {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N) : "memory");
 }
 
 // Offset of the 4-byte scale group (row r, 128-K step 0) in the given layout; nblk4 = K/128.
@@ -246,33 +259,9 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.f;
 
-    block_barrier();  // the previous tile's epilogue is done with LDS
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-      if (s < KT) issue(s, s);
-    int buf = 0;                // buffer of stage kt
-    int fill = NS - 1;          // buffer that stage kt + NS - 1 goes to
-    for (int kt = 0; kt < KT; ++kt) {
-      // stage kt has landed in LDS for every wave; up to NS - 2 later stages stay in flight
-      if (kt + NS - 2 < KT)
-        wait_vm<(NS - 2) * T::LOADS>();
-      else
-        wait_vm<0>();
-      block_barrier();
-      if (kt + NS - 1 < KT) issue(kt + NS - 1, fill);  // refills the buffer read at step kt - 1
-      fill = fill + 1 == NS ? 0 : fill + 1;
-
-      const uint8_t* st = smem + buf * T::STAGE;
-      buf = buf + 1 == NS ? 0 : buf + 1;
-      const uint8_t* a_lds = st;
-      const uint8_t* b_lds = st + T::A_BYTES;
-      const uint32_t* sc = (const uint32_t*)(st + T::A_BYTES + T::B_BYTES);
-      // this lane's scale bytes: byte 0 -> block g (first 64 K), byte 2 -> block 2+g (second 64 K)
-      uint32_t as_sel[T::TM], bs_sel[T::TN];
-#pragma unroll
-      for (int t = 0; t < T::TM; ++t) as_sel[t] = (sc[wm * T::WTM + t * 32 + l32] >> (8 * g)) & 0x00FF00FFu;
-#pragma unroll
-      for (int t = 0; t < T::TN; ++t) bs_sel[t] = (sc[BM + wn * T::WTN + t * 32 + l32] >> (8 * g)) & 0x00FF00FFu;
+    // One 128-K step from LDS: two 64-K halves, each one scaled MFMA per (B block, A block)
+    auto mma_step = [&](const uint8_t* a_lds, const uint8_t* b_lds, const uint32_t* as_sel,
+                        const uint32_t* bs_sel) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         v8i af[T::TM], bf[T::TN];
@@ -300,7 +289,130 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
               acc[x][y] = mfma<2>(bf[x], af[y], acc[x][y], (int)bs_sel[x], (int)as_sel[y]);
           }
       }
-    }
+    };
+
+    if constexpr (T::SPLIT) {
+      static_assert(A_LAYOUT == 1 && B_LAYOUT == 1 && T::TM == 2 && T::TN == 4 && T::WTM == 64 && T::WTN == 128,
+                    "split ring: swizzled scales, 64 x 128 wave tiles");
+#if defined(__HIP_DEVICE_COMPILE__)
+      // In the swizzled layout rows r, r + 32, r + 64, r + 96 of a 128-row group keep their
+      // 4-byte scale groups side by side. A wave's A rows are r0 + l32 and r0 + 32 + l32 with
+      // r0 a multiple of 64 (chunks start on 64-row boundaries), its B rows b0 + l32 + 32t with
+      // b0 a multiple of 128 (EPI_SWIGLU: the wave's 128 gate or up rows, inter a multiple of
+      // 128): one 8-byte and one 16-byte load per lane and step. Rows past the operand read
+      // the zero padding of the 128-row group or, beyond the buffer, 0 (not stored either way).
+      uint8_t* const a_ring = smem;
+      uint8_t* const b_ring = smem + 2 * T::A_BYTES;
+      const uint32_t sa_off = scale_base<1>((uint32_t)(m0 + wm * T::WTM + l32), nblk4);
+      const int b0 = EPI == EPI_SWIGLU ? (wn == 0 ? n0 : sg.inter + n0) : n0 + wn * T::WTN;
+      const uint32_t sb_off = scale_base<1>((uint32_t)(b0 + l32), nblk4);
+      const uint32_t sa_bytes = (uint32_t)((M + 127) / 128 * 128) * nblk4 * 4;
+      const uint32_t sb_bytes = (uint32_t)((N + 127) / 128 * 128) * nblk4 * 4;
+      const __amdgpu_buffer_rsrc_t rsa = make_rsrc(As, sa_bytes), rsb = make_rsrc(Bs, sb_bytes);
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K);
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(B, (uint32_t)N * (uint32_t)K);
+      auto issue_a = [&](int kt) {
+        uint8_t* st = a_ring + (kt & 1) * T::A_BYTES;
+#pragma unroll
+        for (int i = 0; i < T::DA; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + (wave * T::DA + i) * 1024), 16, a_off[i],
+                                                   (uint32_t)kt * BK, 0, 0);
+      };
+      auto issue_b = [&](int kt, int slot) {
+        uint8_t* st = b_ring + slot * T::B_BYTES;
+#pragma unroll
+        for (int i = 0; i < T::DB; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + (wave * T::DB + i) * 1024), 16, b_off[i],
+                                                   (uint32_t)kt * BK, 0, 0);
+      };
+      auto load_scales = [&](int kt, u32x2& sa, u32x4& sb) {
+        const int so = kt * (int)scale_step<1>();
+        sa = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsa, sa_off, so, 0));
+        sb = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsb, sb_off, so, 0));
+      };
+      // Every load of the steady state is issued unconditionally and the last two steps are
+      // peeled: the compiler's own wait before the first use of the scales then counts the
+      // same B loads behind them on every path (vmcnt(DB), as the explicit wait), where a
+      // conditional issue would make it wait for all loads (vmcnt(0)).
+      u32x2 sa;  // scales of the step about to run (loaded one step ahead)
+      u32x4 sb;
+      block_barrier();  // the previous tile's epilogue is done with LDS
+      issue_b(0, 0);
+      issue_a(0);
+      load_scales(0, sa, sb);
+      int bslot = 0;  // B buffer of step kt
+      auto step = [&](int kt, bool next_a, bool next_b) {
+        block_barrier();
+        // this lane's scale bytes: byte 0 -> block g (first 64 K), byte 2 -> block 2+g
+        uint32_t as_sel[2], bs_sel[4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) as_sel[t] = (sa[t] >> (8 * g)) & 0x00FF00FFu;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) bs_sel[t] = (sb[t] >> (8 * g)) & 0x00FF00FFu;
+        // refill the A buffer and the B buffer read at step kt - 1
+        if (next_a) {
+          issue_a(kt + 1);
+          load_scales(kt + 1, sa, sb);
+          // keep the scale loads ahead of the B loads: issued behind them they would be among
+          // the last DB loads, and the next step's wait would also wait for part of B(kt + 2)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (next_b) issue_b(kt + 2, bslot == 0 ? 2 : bslot - 1);
+        const uint8_t* a_lds = a_ring + (kt & 1) * T::A_BYTES;
+        const uint8_t* b_lds = b_ring + bslot * T::B_BYTES;
+        bslot = bslot == 2 ? 0 : bslot + 1;
+        mma_step(a_lds, b_lds, as_sel, bs_sel);
+      };
+      // A(kt), the scales of kt and B(kt) have landed before each step; B(kt + 1) may not have.
+      // A single K step has a path of its own, so that the registers of the last step's scales
+      // come from one place (a merge would have the compiler copy them, and wait for them,
+      // before the step ahead of it is done).
+      if (KT == 1) {
+        wait_vm<0>();
+        step(0, false, false);
+      } else {
+        issue_b(1, 1);
+        for (int kt = 0; kt < KT - 2; ++kt) {
+          wait_vm<T::DB>();
+          step(kt, true, true);
+        }
+        wait_vm<T::DB>();
+        step(KT - 2, true, false);
+        wait_vm<0>();
+        step(KT - 1, false, false);
+      }
+#endif
+    } else {
+      block_barrier();  // the previous tile's epilogue is done with LDS
+#pragma unroll
+      for (int s = 0; s < NS - 1; ++s)
+        if (s < KT) issue(s, s);
+      int buf = 0;                // buffer of stage kt
+      int fill = NS - 1;          // buffer that stage kt + NS - 1 goes to
+      for (int kt = 0; kt < KT; ++kt) {
+        // stage kt has landed in LDS for every wave; up to NS - 2 later stages stay in flight
+        if (kt + NS - 2 < KT)
+          wait_vm<(NS - 2) * T::LOADS>();
+        else
+          wait_vm<0>();
+        block_barrier();
+        if (kt + NS - 1 < KT) issue(kt + NS - 1, fill);  // refills the buffer read at step kt - 1
+        fill = fill + 1 == NS ? 0 : fill + 1;
+
+        const uint8_t* st = smem + buf * T::STAGE;
+        buf = buf + 1 == NS ? 0 : buf + 1;
+        const uint8_t* a_lds = st;
+        const uint8_t* b_lds = st + T::A_BYTES;
+        const uint32_t* sc = (const uint32_t*)(st + T::A_BYTES + T::B_BYTES);
+        // this lane's scale bytes: byte 0 -> block g (first 64 K), byte 2 -> block 2+g (second 64 K)
+        uint32_t as_sel[T::TM], bs_sel[T::TN];
+#pragma unroll
+        for (int t = 0; t < T::TM; ++t) as_sel[t] = (sc[wm * T::WTM + t * 32 + l32] >> (8 * g)) & 0x00FF00FFu;
+#pragma unroll
+        for (int t = 0; t < T::TN; ++t) bs_sel[t] = (sc[BM + wn * T::WTN + t * 32 + l32] >> (8 * g)) & 0x00FF00FFu;
+        mma_step(a_lds, b_lds, as_sel, bs_sel);
+      }
+    }  // main loop
 
     if (EPI == EPI_SWIGLU) {
       // ---- fused epilogue: fp32 gate and up staged in LDS a band of rows at a time, then one
@@ -418,6 +530,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
 
 // Tile configurations: output tile, wave grid, LDS stages.
 using TileL = Tile<256, 256, 4, 2, 2>;  // 8 waves of 64 x 128; large problems
+using TileLR = Tile<256, 256, 4, 2, 2, true>;  // the same with the split ring (swizzled scales)
 using TileN = Tile<256, 192, 4, 2, 2>;  // 8 waves of 64 x 96; when 256 x 256 leaves a round part-empty
 using TileW = Tile<128, 192, 4, 2, 3>;  // 8 waves of 32 x 96
 using TileM = Tile<128, 128, 4, 2, 4>;  // 8 waves of 32 x 64
@@ -497,6 +610,26 @@ hipError_t launch_cfg(const uint8_t* a, const uint8_t* as, int a_layout, const u
   return hipGetLastError();
 }
 
+// The split ring reads the swizzled scales of a wave's rows with single wide loads: both
+// operands' scales swizzled and 16-byte aligned, chunks starting on 64-row boundaries.
+bool split_ring_fits(const uint8_t* as, int a_layout, const uint8_t* bs, int b_layout, int64_t m, int num_chunks) {
+  return a_layout == 1 && b_layout == 1 && (uintptr_t)as % 16 == 0 && (uintptr_t)bs % 16 == 0 &&
+         (num_chunks == 1 || (m / num_chunks) % 64 == 0);
+}
+
+template <int EPI>
+hipError_t launch_split(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs, int64_t m, int64_t n,
+                        int64_t k, uint16_t* c, int64_t ldc, int num_chunks, int first_chunk, int* chunk_done,
+                        hipStream_t stream, SwiGluOut sg = SwiGluOut{}) {
+  using T = TileLR;
+  const int64_t tiles = tile_count(m, n, num_chunks, T::BM, T::BN);
+  const int64_t grid = tiles < device_cu_count() ? tiles : device_cu_count();
+  const int wide = ((uintptr_t)c % 16 == 0 && ldc % 8 == 0) ? 1 : 0;
+  gemm_kernel<T, 1, 1, EPI><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
+      a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done, wide, sg);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 GemmShape gemm_pick_shape(int64_t m, int64_t n, int num_chunks) {
@@ -517,7 +650,12 @@ hipError_t launch_gemm_silu_mul_quant(const uint8_t* a, const uint8_t* as, int a
   const int64_t n = 2 * inter;  // B rows; tile counts match whenever inter is a multiple of BN/2
   hipError_t e;
   switch (pick_config(m, n, 1)) {
-    case CFG_L: e = launch_cfg<TileL, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
+    case CFG_L:
+      if (split_ring_fits(as, a_layout, ws, w_layout, m, 1) && inter % 128 == 0)
+        e = launch_split<EPI_SWIGLU>(a, as, w, ws, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg);
+      else
+        e = launch_cfg<TileL, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg);
+      break;
     case CFG_N: e = launch_cfg<TileN, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
     case CFG_W: e = launch_cfg<TileW, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
     case CFG_M: e = launch_cfg<TileM, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
@@ -534,6 +672,8 @@ hipError_t launch_gemm(const uint8_t* a, const uint8_t* as, int a_layout, const 
                        int64_t ldc, int num_chunks, int first_chunk, int* chunk_done, hipStream_t stream) {
   switch (pick_config(m, n, num_chunks)) {
     case CFG_L:
+      if (split_ring_fits(as, a_layout, bs, b_layout, m, num_chunks))
+        return launch_split<EPI_BF16>(a, as, b, bs, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
       return launch_cfg<TileL>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
     case CFG_N:
       return launch_cfg<TileN>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);

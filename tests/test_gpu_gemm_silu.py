@@ -107,6 +107,32 @@ def test_gemm_silu_mul_quant_workload_rows():
         assert np.array_equal(s_swz[offs], s_lin[r])
 
 
+def test_gemm_silu_mul_quant_split_ring_matches_staged():
+    """With 256 x 256 tiles and swizzled, 16-byte aligned scales the kernel keeps B three
+    stages deep and the scales in registers; scale buffers 4 bytes off that alignment take the
+    staged kernel. Both form the same fp32 sums, so codes and scales agree bit for bit."""
+    m, inter, k = 2048, 3072, 640
+    qa, sa, qw, sw = _operands(m, inter, k, seed_a=11, seed_w=12)
+    outs = []
+    for off in (0, 4):
+        bufs = []
+        for arr in (sa[1], sw[1]):
+            buf = torch.zeros(arr.size + 16, dtype=torch.uint8, device="cuda")
+            view = buf[off:off + arr.size]
+            view.copy_(dev_u8(arr).view(-1))
+            bufs.append(view)
+        assert (bufs[0].data_ptr() % 16 == 0) == (off == 0)
+        q, s_lin, s_swz = mx.gemm_silu_mul_quant(dev_u8(qa), bufs[0], 1, dev_u8(qw), bufs[1], 1, linear=True,
+                                                 swizzled=True)
+        outs.append((q.cpu().numpy(), s_lin.cpu().numpy(), s_swz.cpu().numpy()))
+    for x, y in zip(*outs):
+        assert np.array_equal(x, y)
+    q_ref, s_ref, _, gu = oracle.gemm_silu_mul_quant(qa, sa[1], 1, qw, sw[1], 1, want_gu=True)
+    mass = _mass(qa, sa[1], 1, qw, sw[1], 1, range(m))
+    s_diff, v_diff = silu_mul_quant_check(outs[0][0], outs[0][1], gu, mass, inter)
+    assert s_diff <= 0.01 and v_diff <= 0.01
+
+
 def test_gemm_silu_mul_quant_feeds_down_proj():
     """The fused output is a valid down_proj operand: the GEMM on it equals the GEMM on the
     same codes with scales rebuilt from the linear copy."""
