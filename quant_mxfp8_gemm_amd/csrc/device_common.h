@@ -47,11 +47,13 @@ __device__ __forceinline__ uint32_t cvt_e4m3x4(float a, float b, float c, float 
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
 
-// fp32 -> BF16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+// Two fp32 values -> packed BF16 bits (lo in bits 0-15), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950. On finite inputs (denormals included) it equals the bit-level
+// rounding (u + 0x7FFF + ((u >> 16) & 1)) >> 16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));

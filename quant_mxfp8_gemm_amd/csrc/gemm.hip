@@ -490,8 +490,8 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int c = wn * T::WTN + x * 32 + 8 * q + 4 * g;
-          const uint32_t lo = f32_to_bf16_rne(acc[x][y][4 * q + 0]) | (f32_to_bf16_rne(acc[x][y][4 * q + 1]) << 16);
-          const uint32_t hi = f32_to_bf16_rne(acc[x][y][4 * q + 2]) | (f32_to_bf16_rne(acc[x][y][4 * q + 3]) << 16);
+          const uint32_t lo = pack_bf16x2(acc[x][y][4 * q + 0], acc[x][y][4 * q + 1]);
+          const uint32_t hi = pack_bf16x2(acc[x][y][4 * q + 2], acc[x][y][4 * q + 3]);
           *(uint2*)(smem + r * T::C_STRIDE + c * 2) = make_uint2(lo, hi);
         }
       }

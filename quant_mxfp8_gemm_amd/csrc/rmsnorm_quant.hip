@@ -28,7 +28,7 @@ __device__ __forceinline__ double wave_sum(double v) {
 // values rounded to BF16 equals their exact sum rounded once: fp32 carries more than twice
 // BF16's precision plus two bits, so the intermediate rounding cannot move the result.
 __device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b) {
-  return f32_to_bf16_rne(bf16_lo(a) + bf16_lo(b)) | (f32_to_bf16_rne(bf16_hi(a) + bf16_hi(b)) << 16);
+  return pack_bf16x2(bf16_lo(a) + bf16_lo(b), bf16_hi(a) + bf16_hi(b));
 }
 
 // RES: the row is first replaced by h = BF16(x + res) (written back to res, the residual
