@@ -58,6 +58,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// A lane's value from another lane of its row of 16, by DPP control code (gfx9 encoding).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = dpp_u32<CTRL>((uint32_t)b), hi = dpp_u32<CTRL>((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(lo | (hi << 32)));
+}
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane i of 8 <- lane 7 - i
+constexpr int DPP_MIRROR = 0x140;       // lane i of 16 <- lane 15 - i
+
 // 16-byte streaming load (data read once: do not keep it in the caches).
 __device__ __forceinline__ uint4 load16_stream(const void* p) {
   const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);

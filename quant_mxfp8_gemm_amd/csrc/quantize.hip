@@ -4,7 +4,7 @@
 // quantized input") and of qkv_proj after the all-gather (PR #65496, "Overview").
 //
 // HBM streaming kernel: every lane owns 16-byte pieces (8 BF16) of the input, four neighbouring
-// lanes form one 32-element block, and two xor-shuffles give the block amax. The amax is taken
+// lanes form one 32-element block, and two DPP lane swaps give the block amax. The amax is taken
 // on the BF16 magnitude bits as integers (order-preserving for non-negative floats), the UE8M0
 // exponent comes straight from those bits, and the scaled values (exact power-of-two products)
 // go through the hardware fp32 -> E4M3 conversion, which rounds to nearest even.
@@ -50,8 +50,8 @@ __global__ __launch_bounds__(QT) void quantize_kernel(const uint16_t* __restrict
     uint32_t m = max(max(t.x & 0x7FFFu, (t.x >> 16) & 0x7FFFu), max(t.y & 0x7FFFu, (t.y >> 16) & 0x7FFFu));
     m = max(m, max(max(t.z & 0x7FFFu, (t.z >> 16) & 0x7FFFu), max(t.w & 0x7FFFu, (t.w >> 16) & 0x7FFFu)));
     // the four lanes of a block are all in range or all out of range (total % 4 == 0)
-    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+    m = max(m, dpp_u32<DPP_XOR1>(m));
+    m = max(m, dpp_u32<DPP_XOR2>(m));
     const uint32_t s = ue8m0_from_amax_bf16_bits(m);
     const float f = inv_scale_from_ue8m0(s);
     const uint32_t lo = cvt_e4m3x4(bf16_lo(t.x) * f, bf16_hi(t.x) * f, bf16_lo(t.y) * f, bf16_hi(t.y) * f);

@@ -18,9 +18,15 @@ namespace {
 
 constexpr int RT = 256;  // threads per workgroup (4 waves)
 
+// Sum over the 64 lanes, in every lane: four DPP steps inside each row of 16 lanes, then two
+// cross-row exchanges.
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  v += dpp_f64<DPP_XOR1>(v);
+  v += dpp_f64<DPP_XOR2>(v);
+  v += dpp_f64<DPP_HALF_MIRROR>(v);
+  v += dpp_f64<DPP_MIRROR>(v);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
   return v;
 }
 
@@ -54,29 +60,40 @@ __global__ __launch_bounds__(RT) void rmsnorm_quant_kernel(const uint16_t* __res
     const int c8 = u * RT + (int)threadIdx.x;
     wv[u] = c8 < cpr ? *(const uint4*)(w + c8 * 8) : make_uint4(0u, 0u, 0u, 0u);
   }
-  double ss = 0.0;
+  // every load of the row is in flight before the first one is used
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
     const int c8 = u * RT + (int)threadIdx.x;
-    if (c8 < cpr) {
-      v[u] = *(const uint4*)(xr + c8 * 8);
-      if (RES) {
-        uint16_t* rp = res + row * ldr + c8 * 8;
-        const uint4 rv = *(const uint4*)rp;
-        v[u] = make_uint4(add_bf16x2(v[u].x, rv.x), add_bf16x2(v[u].y, rv.y), add_bf16x2(v[u].z, rv.z),
-                          add_bf16x2(v[u].w, rv.w));
-        *(uint4*)rp = v[u];
-      }
-      const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    v[u] = c8 < cpr ? *(const uint4*)(xr + c8 * 8) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (RES) {
+    uint4 rv[CPT];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const double a = (double)bf16_lo(wd[j]);
-        const double b = (double)bf16_hi(wd[j]);
-        ss += a * a;
-        ss += b * b;
-      }
-    } else {
-      v[u] = make_uint4(0u, 0u, 0u, 0u);
+    for (int u = 0; u < CPT; ++u) {
+      const int c8 = u * RT + (int)threadIdx.x;
+      rv[u] = c8 < cpr ? *(const uint4*)(res + row * ldr + c8 * 8) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    // all sums before the first store: a load waited for after a store would wait for it too
+#pragma unroll
+    for (int u = 0; u < CPT; ++u)
+      v[u] = make_uint4(add_bf16x2(v[u].x, rv[u].x), add_bf16x2(v[u].y, rv[u].y), add_bf16x2(v[u].z, rv[u].z),
+                        add_bf16x2(v[u].w, rv[u].w));
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+      const int c8 = u * RT + (int)threadIdx.x;
+      if (c8 < cpr) *(uint4*)(res + row * ldr + c8 * 8) = v[u];
+    }
+  }
+  double ss = 0.0;  // pad lanes hold zeros
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const uint32_t wd[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double a = (double)bf16_lo(wd[j]);
+      const double b = (double)bf16_hi(wd[j]);
+      ss += a * a;
+      ss += b * b;
     }
   }
   ss = wave_sum(ss);
@@ -107,8 +124,8 @@ __global__ __launch_bounds__(RT) void rmsnorm_quant_kernel(const uint16_t* __res
 #pragma unroll
       for (int j = 0; j < 8; ++j) y[j] = 0.f;
     }
-    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+    m = max(m, dpp_u32<DPP_XOR1>(m));  // the four lanes of a 32-block
+    m = max(m, dpp_u32<DPP_XOR2>(m));
     const uint32_t s = ue8m0_from_amax_f32_bits(m);
     const float f = inv_scale_from_ue8m0(s);
     if (live) {
