@@ -136,8 +136,8 @@ def cpu_baseline(target_s):
 def main():
     args = _parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the reduce-scatter that would follow the chunked GEMM is out of scope).", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the reduce-scatter that would follow the chunked GEMM is not part of it).", file=sys.stderr)
         sys.exit(2)
 
     import torch
