@@ -13,9 +13,16 @@
 //    tall, so the 32 tiles an XCD works on at once share A and B panels in its L2.
 //  * Large problems use a 256 x 256 output tile split over 8 waves as 4 x 2; each wave owns
 //    64 x 128, i.e. 2 x 4 blocks of V_MFMA_SCALE_F32_32X32X64_F8F6F4 accumulated in fp32.
-//    Two waves share each SIMD, so one issues MFMAs while the other waits on LDS. Problems
-//    with too few such tiles to fill the chip (few rows per chunk) use 128 x 128, 64 x 128
-//    or 32 x 128 tiles with four LDS stages, so three stages of loads are in flight.
+//    Two waves share each SIMD, so one issues MFMAs while the other waits on LDS. Smaller
+//    tiles (256 x 192, 128 x 192, 128 x 128, 64 x 128, 32 x 128, with two to four LDS stages)
+//    serve problems with fewer rows per chunk; the tile is the one with the shortest
+//    estimated makespan (rounds of workgroups over the CUs times the cost of a K step).
+//  * With swizzled, 16-byte aligned scales the 256 x 256 tile runs a split ring: A in two
+//    stage buffers and B in three (B fetched two steps ahead, all 160 KiB of LDS), the scales
+//    of a wave's rows loaded one step ahead into registers with one 8-byte and one 16-byte
+//    load (rows r, r+32, r+64, r+96 of a swizzled 128-row group are adjacent). Every other
+//    case uses NS-stage buffers holding A, B and the scale dwords together. Both give the same
+//    bits: every configuration sums the same MFMA partials in the same order.
 //  * The instruction applies the UE8M0 block scales itself. Operand layout (32 rows x 64 K):
 //    lane l holds row l%32; with g = l/32, its bytes 0..15 are K 16g..16g+15 and bytes 16..31
 //    are K 32+16g..32+16g+15. The scale of (row r, 32-block b) comes from lane r + 32b, byte
@@ -25,7 +32,7 @@
 //  * K advances 128 bytes per stage (one full 128-byte line per row). The stages of A, B and
 //    their scale dwords live in LDS and are filled straight from memory by LDS-DMA loads:
 //    buffer_load_dwordx4 ... lds for A and B (a 32-bit row offset per lane, the stage's K
-//    offset in a scalar register), global_load_lds_dword for the scales. Each load
+//    offset in a scalar register), global_load_lds_dword for the staged scales. Each load
 //    instruction moves 8 whole rows (8 lanes per 128-byte line). A row of a stage is 8
 //    chunks of 16 bytes; chunk c of row r sits in slot c ^ ((r ^ (r >> 3)) & 7), so the rows
 //    read by one ds_read_b128 spread over all banks. The 4 scale bytes of a row for one
