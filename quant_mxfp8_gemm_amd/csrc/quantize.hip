@@ -17,7 +17,7 @@ namespace mxfp8 {
 namespace {
 
 constexpr int QT = 256;  // threads per workgroup
-constexpr int QU = 4;    // 16-byte pieces per lane
+constexpr int QU = 2;    // 16-byte pieces per lane
 
 template <typename Idx, bool LIN, bool SWZ>
 __global__ __launch_bounds__(QT) void quantize_kernel(const uint16_t* __restrict__ x, Idx rows, Idx k,
