@@ -182,6 +182,8 @@ int mxfp8_swizzle_scales_check(const void* scales_linear, int64_t rows, int64_t 
  *   mxfp8_gemm_tiles_per_chunk(m, n, num_chunks). This is the hook a reduce-scatter
  *   would wait on.
  * The result does not depend on num_chunks, first_chunk or chunk_done.
+ * Performance: large problems run fastest with both scale buffers in the swizzled layout,
+ * 16-byte aligned, and m/num_chunks a multiple of 64 (the output is the same bits either way).
  */
 int mxfp8_gemm_bf16out(const void* a_e4m3, const void* a_scales, int a_scale_layout,
                        const void* b_e4m3, const void* b_scales, int b_scale_layout, int64_t m,
