@@ -53,8 +53,8 @@ def _parse():
 # counter of a 1 GiB copy onto 1 GiB. Valid only for the kernel code it was taken on
 # (gemm_code_sha256).
 GEMM_TRAFFIC = {
-    "source_sha256": "b386d7064c5b25a5fe38ec3fcb2f479aae8f951659e32856759d34798659acdd",
-    "fetch_kib": 456272.6, "write_kib": 393462.8,
+    "source_sha256": "53b9a04fa714489c38254794c6c21ab97c347a7d86baa42304e901238d5d7a82",
+    "fetch_kib": 456267.6, "write_kib": 393493.6,
     "fetch_factor": 2.0, "write_factor": 1.0,
 }
 

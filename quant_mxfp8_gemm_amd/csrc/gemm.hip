@@ -266,24 +266,38 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.f;
 
+    // Fragment offsets inside a stage: the swizzle of row r + 32 t is that of row r with bit 2
+    // flipped when t is odd (which swaps the two 64-K halves of the row), so four per-lane
+    // offsets per operand, relative to the wave's first row, address every fragment read; the
+    // rest is a constant (t * 32 rows).
+    int oa[2][2], ob[2][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        oa[kk][h] = lds_off(wm * T::WTM + l32, 4 * kk + 2 * h + g) - wm * T::WTM * 128;
+        ob[kk][h] = lds_off(wn * T::WTN + l32, 4 * kk + 2 * h + g) - wn * T::WTN * 128;
+      }
     // One 128-K step from LDS: two 64-K halves, each one scaled MFMA per (B block, A block)
     auto mma_step = [&](const uint8_t* a_lds, const uint8_t* b_lds, const uint32_t* as_sel,
                         const uint32_t* bs_sel) {
+      const uint8_t* const a_w = a_lds + wm * T::WTM * 128;
+      const uint8_t* const b_w = b_lds + wn * T::WTN * 128;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         v8i af[T::TM], bf[T::TN];
 #pragma unroll
         for (int t = 0; t < T::TM; ++t) {
-          const int r = wm * T::WTM + t * 32 + l32;
-          const v4i lo = *(const v4i*)(a_lds + lds_off(r, 4 * ks + g));
-          const v4i hi = *(const v4i*)(a_lds + lds_off(r, 4 * ks + 2 + g));
+          const int kk = ks ^ (t & 1);
+          const v4i lo = *(const v4i*)(a_w + oa[kk][0] + t * 32 * 128);
+          const v4i hi = *(const v4i*)(a_w + oa[kk][1] + t * 32 * 128);
           af[t] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
 #pragma unroll
         for (int t = 0; t < T::TN; ++t) {
-          const int r = wn * T::WTN + t * 32 + l32;
-          const v4i lo = *(const v4i*)(b_lds + lds_off(r, 4 * ks + g));
-          const v4i hi = *(const v4i*)(b_lds + lds_off(r, 4 * ks + 2 + g));
+          const int kk = ks ^ (t & 1);
+          const v4i lo = *(const v4i*)(b_w + ob[kk][0] + t * 32 * 128);
+          const v4i hi = *(const v4i*)(b_w + ob[kk][1] + t * 32 * 128);
           bf[t] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
 #pragma unroll
