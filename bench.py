@@ -53,8 +53,8 @@ def _parse():
 # counter of a 1 GiB copy onto 1 GiB. Valid only for the kernel code it was taken on
 # (gemm_code_sha256).
 GEMM_TRAFFIC = {
-    "source_sha256": "53b9a04fa714489c38254794c6c21ab97c347a7d86baa42304e901238d5d7a82",
-    "fetch_kib": 456267.6, "write_kib": 393493.6,
+    "source_sha256": "64553a22ce283a30d1e9a04eaa69f14be846515163c395a489fe84bb8c822fb8",
+    "fetch_kib": 456331.1, "write_kib": 393421.1,
     "fetch_factor": 2.0, "write_factor": 1.0,
 }
 

@@ -156,7 +156,8 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // wave-uniform (an SGPR): the LDS-DMA destinations and M0 are formed with scalar instructions
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / (BN / T::WTN), wn = wave % (BN / T::WTN);
   const int l32 = lane & 31, g = lane >> 5;
 
