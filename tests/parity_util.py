@@ -69,6 +69,25 @@ GEMM_REL_TOL = 2e-2
 MFMA_MASS_ERR = 4e-5
 
 
+def gemm_mass_bound_ratio(c_bits: np.ndarray, ref_bits: np.ndarray, exact: np.ndarray, abs_sum: np.ndarray) -> float:
+    """Largest |c - r| / (MFMA_MASS_ERR * S + ulp) over the elements: c the kernel's BF16
+    output, r the oracle's BF16 rounding of the exact sum, S = sum_k |A_mk B_nk|, ulp the BF16
+    spacing at the larger of |exact| and |c|. The kernel's fp32 sum lies within MFMA_MASS_ERR * S
+    of the exact one and BF16 rounding moves each side by at most half a spacing, so a correct
+    kernel gives a ratio <= 1 whatever the cancellation; a misapplied block scale or operand gives
+    an error of the order of S. Used where inputs cancel far below a thousandth of their mass,
+    which the relative bar with its 1e-3 S floor is not meant for."""
+    c = bf16_bits_to_f64(c_bits)
+    r = bf16_bits_to_f64(ref_bits)
+    x = np.maximum(np.abs(np.asarray(exact, dtype=np.float64)), np.abs(c))
+    s = np.asarray(abs_sum, dtype=np.float64)
+    if r.size == 0:
+        return 0.0
+    with np.errstate(divide="ignore"):
+        ulp = np.where(x > 0, np.exp2(np.floor(np.log2(np.where(x > 0, x, 1.0))) - 7), 2.0 ** -133)
+    return float(np.max(np.abs(c - r) / (MFMA_MASS_ERR * s + ulp)))
+
+
 def _scale_exp(amax: np.ndarray) -> np.ndarray:
     """Elementwise smallest e in [-127, 127] with amax <= 448 * 2^e (amax 0 -> -127)."""
     a = np.asarray(amax, dtype=np.float64)

@@ -17,7 +17,7 @@ import torch
 import oracle
 import quant_mxfp8_gemm_amd as mx
 import synth
-from parity_util import GEMM_REL_TOL, bf16_bits_to_f64, bits16, dev_u8, gemm_rel_error
+from parity_util import GEMM_REL_TOL, bf16_bits_to_f64, bits16, dev_u8, gemm_mass_bound_ratio, gemm_rel_error
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +59,14 @@ def _assert_close(c_bits, ref_bits, abs_sum, what):
     rel, norm, per_mass = gemm_rel_error(c_bits, ref_bits, abs_sum)
     print(f"{what}: max rel err {rel:.3e}, normwise {norm:.3e}, max err / sum|ab| {per_mass:.3e}", flush=True)
     assert rel <= GEMM_REL_TOL, what
+
+
+def _assert_mass_bound(c_bits, ref_bits, exact, abs_sum, what):
+    rel, norm, per_mass = gemm_rel_error(c_bits, ref_bits, abs_sum)
+    ratio = gemm_mass_bound_ratio(c_bits, ref_bits, exact, abs_sum)
+    print(f"{what}: max err / (4e-5 S + ulp) {ratio:.3f}, max err / S {per_mass:.3e}, max rel err {rel:.3e}",
+          flush=True)
+    assert ratio <= 1.0, what
 
 
 def _abs_sum_full(qa, sa, la, qb, sb, lb):
@@ -170,7 +178,7 @@ def test_gemm_o_proj_m128_full():
 def _sample_indices(m, n, chunks, rng, count=6000):
     rows = [0, m - 1] + [c * (m // chunks) for c in range(chunks)] + [c * (m // chunks) - 1 for c in range(1, chunks)]
     rows += [r for r in (255, 256, 511, 512) if r < m]
-    cols = [0, n - 1, 255, 256, 4095, 4096]
+    cols = [cc for cc in (0, n - 1, 255, 256, 4095, 4096) if cc < n]
     ri = [rng.integers(0, m, count)]
     ci = [rng.integers(0, n, count)]
     for r in rows:  # whole rows at chunk and tile edges
@@ -264,3 +272,70 @@ def test_chain_quantize_then_gemm_m32768(k):
     ref, _ = oracle.gemm_sampled(qa_ref, sa_ref, 1, qb_ref, sb_ref, 1, ri, ci)
     _assert_close(bits16(c)[ri, ci], ref, _abs_sum_sampled(qa_ref, sa_ref, 1, qb_ref, sb_ref, 1, ri, ci),
                   f"chain k={k}")
+
+
+
+def _wide_scale_operands(m, n, k, seed, ones=False):
+    """E4M3 codes of quantised N(0, 1) activations and N(0, 0.02) weights (or all 1.0) with
+    their per-32-block UE8M0 scales replaced by codes spread over nearly the whole range
+    (2..252, so bit 7 of the scale byte is exercised both ways): block kb of A rows gets
+    base_kb + d_m and of B rows 254 - base_kb + d_n with |d| <= 8, so a product's scale
+    2^(sa + sb - 254) lies in 2^-16..2^16, the blocks of one MFMA can differ by up to 2^32, and
+    every sum stays finite and normal in fp32. Blocks this far apart cancel much more deeply than
+    the workloads' (|C| down to 1e-4 of its mass S), where the relative bar's 1e-3 S floor would
+    turn the MFMA's accumulation error (up to 4e-5 S) into 4e-2; these tests therefore hold every
+    element to |c - r| <= 4e-5 S + one BF16 spacing, which any misapplied scale exceeds by orders
+    of magnitude."""
+    rng = np.random.default_rng(seed)
+    nblk = k // 32
+    if ones:
+        qa = np.full((m, k), 0x38, np.uint8)
+        qb = np.full((n, k), 0x38, np.uint8)
+    else:
+        qa, _, _ = oracle.quantize(bits16(synth.activations_bf16(m, k, seed=seed)))
+        qb, _, _ = oracle.quantize(bits16(synth.weights_bf16(n, k, seed=seed + 1)))
+    base = rng.integers(10, 245, nblk)
+    sa = np.clip(base[None, :] + rng.integers(-8, 9, (m, nblk)), 2, 252).astype(np.uint8)
+    sb = np.clip(254 - base[None, :] + rng.integers(-8, 9, (n, nblk)), 2, 252).astype(np.uint8)
+    assert sa.max() >= 128 and sa.min() < 128 and sb.max() >= 128 and sb.min() < 128
+    return qa, {mx.LINEAR: sa, mx.SWIZZLED: oracle.swizzle_scales(sa)}, qb, \
+        {mx.LINEAR: sb, mx.SWIZZLED: oracle.swizzle_scales(sb)}
+
+
+@pytest.mark.parametrize("la,lb", [(0, 0), (1, 1), (0, 1)])
+@pytest.mark.parametrize("m,n,k,chunks", [(300, 520, 512, 1), (132, 6100, 256, 4), (760, 1000, 384, 4)])
+def test_gemm_wide_scale_range_full(m, n, k, chunks, la, lb):
+    """Scale codes across the UE8M0 range, not only the 110-127 that quantised N(0, 1) and
+    N(0, 0.02) data produce; compared in full."""
+    print(f"gemm wide scales m={m} n={n} k={k} chunks={chunks} layouts={la}{lb}", flush=True)
+    qa, sa, qb, sb = _wide_scale_operands(m, n, k, seed=m * 31 + k)
+    ref, exact = oracle.gemm(qa, sa[la], la, qb, sb[lb], lb, want_f64=True)
+    c = _gpu_gemm(qa, sa[la], la, qb, sb[lb], lb, num_chunks=chunks)
+    _assert_mass_bound(c, ref, exact, _abs_sum_full(qa, sa[la], la, qb, sb[lb], lb), f"wide scales m={m} n={n} k={k}")
+
+
+def test_gemm_wide_scale_range_closed_form():
+    """All codes 1.0 with the wide scales: C[m,n] = 32 sum_kb 2^(sa + sb - 254), a sum of powers
+    of two spanning 2^32, held to the same bar (the fp32 sum keeps 24 bits of it, so the BF16
+    result is the exact one or its neighbour)."""
+    m, n, k = 256, 384, 1024
+    qa, sa, qb, sb = _wide_scale_operands(m, n, k, seed=3, ones=True)
+    want = 32.0 * np.exp2(sa[0].astype(np.int64)[:, None, :] + sb[0].astype(np.int64)[None, :, :] - 254).sum(-1)
+    ref = oracle.gemm(qa, sa[0], 0, qb, sb[0], 0)
+    assert np.array_equal(ref, oracle.bf16_from_double(want.ravel()).reshape(m, n))
+    c = _gpu_gemm(qa, sa[1], 1, qb, sb[0], 0)
+    _assert_close(c, ref, want, "wide scales, all codes 1.0")
+
+
+def test_gemm_wide_scale_range_split_ring():
+    """The same on the 256 x 256 split-ring kernel (swizzled, 16-byte aligned scales in
+    registers), compared on sampled outputs."""
+    m, n, k, chunks = 4096, 4096, 512, 4
+    assert mx.gemm_tiles_per_chunk(m, n, chunks) == 4 * 16
+    qa, sa, qb, sb = _wide_scale_operands(m, n, k, seed=11)
+    c = _gpu_gemm(qa, sa[1], 1, qb, sb[1], 1, num_chunks=chunks)
+    rng = np.random.default_rng(12)
+    ri, ci = _sample_indices(m, n, chunks, rng)
+    ref, exact = oracle.gemm_sampled(qa, sa[1], 1, qb, sb[1], 1, ri, ci)
+    _assert_mass_bound(c[ri, ci], ref, exact, _abs_sum_sampled(qa, sa[1], 1, qb, sb[1], 1, ri, ci),
+                       "wide scales split ring")
