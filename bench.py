@@ -53,8 +53,8 @@ def _parse():
 # counter of a 1 GiB copy onto 1 GiB. Valid only for the kernel code it was taken on
 # (gemm_code_sha256).
 GEMM_TRAFFIC = {
-    "source_sha256": "64553a22ce283a30d1e9a04eaa69f14be846515163c395a489fe84bb8c822fb8",
-    "fetch_kib": 456331.1, "write_kib": 393421.1,
+    "source_sha256": "e4f960efe807c0969bd154dd8f85f7e3600b22eb522316e9e2aecf13956b8d7c",
+    "fetch_kib": 456268.1, "write_kib": 393441.8,
     "fetch_factor": 2.0, "write_factor": 1.0,
 }
 
