@@ -14,9 +14,10 @@
 //  * Large problems use a 256 x 256 output tile split over 8 waves as 4 x 2; each wave owns
 //    64 x 128, i.e. 2 x 4 blocks of V_MFMA_SCALE_F32_32X32X64_F8F6F4 accumulated in fp32.
 //    Two waves share each SIMD, so one issues MFMAs while the other waits on LDS. Smaller
-//    tiles (256 x 192, 192 x 192 on 6 waves, 128 x 192, 128 x 128, 64 x 128, 32 x 128, with two
-//    to four LDS stages) serve problems with fewer rows per chunk; the tile is the one with the
-//    shortest estimated makespan (rounds of workgroups over the CUs times the cost of a K step).
+//    tiles (256 x 192, 192 x 192 and 96 x 192 on 6 waves, 128 x 192, 128 x 128, 64 x 128,
+//    32 x 128, with two to four LDS stages) serve problems with fewer rows per chunk; the tile is
+//    the one with the shortest estimated makespan (rounds of workgroups over the CUs times the
+//    measured time of its K step).
 //  * With swizzled, 16-byte aligned scales the 256 x 256 tile runs a split ring: A in two
 //    stage buffers and B in three (B fetched two steps ahead, all 160 KiB of LDS), the scales
 //    of a wave's rows loaded one step ahead into registers with one 8-byte and one 16-byte
@@ -556,6 +557,7 @@ using TileLR = Tile<256, 256, 4, 2, 2, true>;  // the same with the split ring (
 using TileN = Tile<256, 192, 4, 2, 2>;  // 8 waves of 64 x 96; when 256 x 256 leaves a round part-empty
 using TileW = Tile<128, 192, 4, 2, 3>;  // 8 waves of 32 x 96
 using TileQ = Tile<192, 192, 3, 2, 3>;  // 6 waves of 64 x 96
+using TileR = Tile<96, 192, 3, 2, 4>;   // 6 waves of 32 x 96
 using TileM = Tile<128, 128, 4, 2, 4>;  // 8 waves of 32 x 64
 using TileS = Tile<64, 128, 2, 4, 4>;   // 8 waves of 32 x 32
 using TileT = Tile<32, 128, 1, 4, 4>;   // 4 waves of 32 x 32; a few rows per chunk
@@ -578,21 +580,20 @@ int64_t tile_count(int64_t m, int64_t n, int num_chunks, int bm, int bn) {
   return (int64_t)num_chunks * ((m / num_chunks + bm - 1) / bm) * ((n + bn - 1) / bn);
 }
 
-enum { CFG_L, CFG_N, CFG_Q, CFG_W, CFG_M, CFG_S, CFG_T };
+enum { CFG_L, CFG_N, CFG_Q, CFG_W, CFG_R, CFG_M, CFG_S, CFG_T };
 
 // Tile choice by estimated makespan: rounds of workgroups over the compute units times the
-// time of one tile. A tile's K step costs its MFMA work (BM x BN; 256 x 192 charged 5% for
-// its lower reuse per loaded byte) but no less than a latency floor measured at about the
-// work of a 256 x 256 step / 2.25: below that a workgroup waits on its loads and barriers,
-// not on the MFMAs. Among equal estimates the configuration with more tiles wins (more
-// workgroups in flight). A tile must fit in a chunk's rows.
+// time of one tile's 128-K step, measured per configuration on MI355X (N = 6144 sweeps, in
+// microseconds; smaller tiles take less time per step but need more rounds). Among equal
+// estimates the configuration with more tiles wins (more workgroups in flight). A tile must
+// fit in a chunk's rows (the 32-row tile takes any chunk).
 struct CfgInfo {
   int id, bm, bn;
-  double charge;
+  double step_us;
 };
-constexpr CfgInfo kCfgs[] = {{CFG_L, 256, 256, 1.0},  {CFG_N, 256, 192, 1.05}, {CFG_Q, 192, 192, 1.0}, {CFG_W, 128, 192, 1.0},
-                             {CFG_M, 128, 128, 1.0},  {CFG_S, 64, 128, 1.0},   {CFG_T, 32, 128, 1.0}};
-constexpr double kStepFloor = 256.0 * 256.0 / 2.25;
+constexpr CfgInfo kCfgs[] = {{CFG_L, 256, 256, 2.0},  {CFG_N, 256, 192, 2.0},  {CFG_Q, 192, 192, 1.67},
+                             {CFG_W, 128, 192, 1.23}, {CFG_R, 96, 192, 1.10},  {CFG_M, 128, 128, 0.96},
+                             {CFG_S, 64, 128, 0.73},  {CFG_T, 32, 128, 0.40}};
 
 int pick_config(int64_t m, int64_t n, int num_chunks) {
   const int64_t rows = m / num_chunks;
@@ -602,8 +603,7 @@ int pick_config(int64_t m, int64_t n, int num_chunks) {
   for (const CfgInfo& c : kCfgs) {
     if (c.id != CFG_T && rows < c.bm) continue;  // the 32-row tile takes any chunk
     const int64_t tiles = tile_count(m, n, num_chunks, c.bm, c.bn);
-    const double step = (double)c.bm * c.bn * c.charge;
-    const double span = (double)((tiles + REF_CUS - 1) / REF_CUS) * (step > kStepFloor ? step : kStepFloor);
+    const double span = (double)((tiles + REF_CUS - 1) / REF_CUS) * c.step_us;
     if (best_tiles == 0 || span < best_span * 0.999 || (span <= best_span * 1.001 && tiles > best_tiles)) {
       best = c.id;
       best_span = span;
@@ -660,6 +660,7 @@ GemmShape gemm_pick_shape(int64_t m, int64_t n, int num_chunks) {
     case CFG_L: return GemmShape{TileL::BM, TileL::BN};
     case CFG_N: return GemmShape{TileN::BM, TileN::BN};
     case CFG_Q: return GemmShape{TileQ::BM, TileQ::BN};
+    case CFG_R: return GemmShape{TileR::BM, TileR::BN};
     case CFG_W: return GemmShape{TileW::BM, TileW::BN};
     case CFG_M: return GemmShape{TileM::BM, TileM::BN};
     case CFG_S: return GemmShape{TileS::BM, TileS::BN};
@@ -682,6 +683,7 @@ hipError_t launch_gemm_silu_mul_quant(const uint8_t* a, const uint8_t* as, int a
       break;
     case CFG_N: e = launch_cfg<TileN, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
     case CFG_Q: e = launch_cfg<TileQ, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
+    case CFG_R: e = launch_cfg<TileR, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
     case CFG_W: e = launch_cfg<TileW, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
     case CFG_M: e = launch_cfg<TileM, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
     case CFG_S: e = launch_cfg<TileS, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
@@ -704,6 +706,8 @@ hipError_t launch_gemm(const uint8_t* a, const uint8_t* as, int a_layout, const 
       return launch_cfg<TileN>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
     case CFG_Q:
       return launch_cfg<TileQ>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
+    case CFG_R:
+      return launch_cfg<TileR>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
     case CFG_W:
       return launch_cfg<TileW>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
     case CFG_M:

@@ -178,5 +178,7 @@ def test_tiles_per_chunk(lib):
     assert mx.gemm_tiles_per_chunk(512, 6144, 4) == 1 * 48       # 128 x 128
     assert mx.gemm_tiles_per_chunk(4096, 6144, 4) == 4 * 32      # 256 x 192: two full rounds
     assert mx.gemm_tiles_per_chunk(3072, 6144, 4) == 4 * 32      # 192 x 192: 768 rows per chunk, no empty rows
+    assert mx.gemm_tiles_per_chunk(3000, 6144, 4) == 4 * 32      # 192 x 192 (256 x 192 would give 3 x 32)
+    assert mx.gemm_tiles_per_chunk(700, 6144, 4) == 2 * 32       # 96 x 192 for 175 rows (128 x 128 would give 2 x 48)
     assert mx.gemm_tiles_per_chunk(256, 6144, 1) == 4 * 48       # 64 x 128
     assert mx.gemm_tiles_per_chunk(128, 6144, 1) == 4 * 48       # 32 x 128

@@ -104,7 +104,7 @@ def test_gemm_small_full(m, n, k, chunks, la, lb):
 # One shape per tile configuration (the kernel picks the tile from the rows per chunk and the
 # tile count), each with ragged M and N tails: (m, n, k, chunks, tile_m, tile_n).
 TILE_CASES = [(2000, 8000, 256, 1, 256, 256), (1000, 12200, 256, 1, 256, 192), (3000, 6100, 256, 4, 192, 192),
-              (760, 6100, 256, 4, 128, 192),
+              (1016, 6100, 256, 4, 128, 192), (760, 6100, 256, 4, 96, 192),
               (200, 12250, 256, 1, 128, 128),
               (100, 12200, 256, 1, 64, 128), (132, 6100, 256, 4, 32, 128)]
 

@@ -52,9 +52,9 @@ def _mass(qa, sa, la, qw, sw, lw, rows):
 
 
 # (m, inter, k, tile_m): one case per tile configuration (256 x 256, 256 x 192, 192 x 192,
-# 128 x 192, 128 x 128, 64 x 128, 32 x 128), with ragged rows and columns
-CASES = [(2048, 4096, 128, 256), (2048, 3072, 256, 256), (1500, 3072, 256, 192), (768, 3072, 256, 128),
-         (1000, 1536, 256, 128),
+# 128 x 192, 96 x 192, 128 x 128, 64 x 128, 32 x 128), with ragged rows and columns
+CASES = [(2048, 4096, 128, 256), (2048, 3072, 256, 256), (1500, 3072, 256, 192), (1024, 3072, 256, 128),
+         (768, 3072, 256, 96), (1000, 1536, 256, 128),
          (100, 6112, 256, 64), (40, 1056, 256, 32)]
 
 
