@@ -53,8 +53,8 @@ def _parse():
 # counter of a 1 GiB copy onto 1 GiB. Valid only for the kernel code it was taken on
 # (gemm_code_sha256).
 GEMM_TRAFFIC = {
-    "source_sha256": "f1d209b7c1aecdb88223bbd1e0a4e2740a33d840d650e27a0ae717b0c6678ed6",
-    "fetch_kib": 456268.1, "write_kib": 393473.7,
+    "source_sha256": "15c76a823bad1bfba19e6b32edf1d1bd27095705fc4b6ed968aad838b32b8481",
+    "fetch_kib": 456266.1, "write_kib": 393467.4,
     "fetch_factor": 2.0, "write_factor": 1.0,
 }
 

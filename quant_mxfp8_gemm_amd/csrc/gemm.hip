@@ -285,6 +285,8 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
                         const uint32_t* bs_sel) {
       const uint8_t* const a_w = a_lds + wm * T::WTM * 128;
       const uint8_t* const b_w = b_lds + wn * T::WTN * 128;
+      // the compiler's predefined LDS-read / MFMA interleave (strategy 0) for this region
+      __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         v8i af[T::TM], bf[T::TN];
