@@ -53,8 +53,8 @@ def _parse():
 # counter of a 1 GiB copy onto 1 GiB. Valid only for the kernel code it was taken on
 # (gemm_code_sha256).
 GEMM_TRAFFIC = {
-    "source_sha256": "15c76a823bad1bfba19e6b32edf1d1bd27095705fc4b6ed968aad838b32b8481",
-    "fetch_kib": 456266.1, "write_kib": 393467.4,
+    "source_sha256": "eb25858e259c3601a4116caa9b68fd904cc132ae9da6dcd3e27338b615ff3a09",
+    "fetch_kib": 456326.3, "write_kib": 393677.5,
     "fetch_factor": 2.0, "write_factor": 1.0,
 }
 

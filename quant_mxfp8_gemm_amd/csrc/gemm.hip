@@ -280,9 +280,10 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
         oa[kk][h] = lds_off(wm * T::WTM + l32, 4 * kk + 2 * h + g) - wm * T::WTM * 128;
         ob[kk][h] = lds_off(wn * T::WTN + l32, 4 * kk + 2 * h + g) - wn * T::WTN * 128;
       }
-    // One 128-K step from LDS: two 64-K halves, each one scaled MFMA per (B block, A block)
+    // One 128-K step from LDS: two 64-K halves, each one scaled MFMA per (B block, A block);
+    // between_halves runs after the first half's MFMAs are issued
     auto mma_step = [&](const uint8_t* a_lds, const uint8_t* b_lds, const uint32_t* as_sel,
-                        const uint32_t* bs_sel) {
+                        const uint32_t* bs_sel, auto&& between_halves) {
       const uint8_t* const a_w = a_lds + wm * T::WTM * 128;
       const uint8_t* const b_w = b_lds + wn * T::WTN * 128;
       // the compiler's predefined LDS-read / MFMA interleave (strategy 0) for this region
@@ -313,6 +314,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
             else
               acc[x][y] = mfma<2>(bf[x], af[y], acc[x][y], (int)bs_sel[x], (int)as_sel[y]);
           }
+        if (ks == 0) between_halves();
       }
     };
 
@@ -374,19 +376,22 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
         for (int t = 0; t < 2; ++t) as_sel[t] = (sa[t] >> (8 * g)) & 0x00FF00FFu;
 #pragma unroll
         for (int t = 0; t < 4; ++t) bs_sel[t] = (sb[t] >> (8 * g)) & 0x00FF00FFu;
-        // refill the A buffer and the B buffer read at step kt - 1
-        if (next_a) {
-          issue_a(kt + 1);
-          load_scales(kt + 1, sa, sb);
-          // keep the scale loads ahead of the B loads: issued behind them they would be among
-          // the last DB loads, and the next step's wait would also wait for part of B(kt + 2)
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if (next_b) issue_b(kt + 2, bslot == 0 ? 2 : bslot - 1);
+        const int refill = bslot == 0 ? 2 : bslot - 1;
         const uint8_t* a_lds = a_ring + (kt & 1) * T::A_BYTES;
         const uint8_t* b_lds = b_ring + bslot * T::B_BYTES;
         bslot = bslot == 2 ? 0 : bslot + 1;
-        mma_step(a_lds, b_lds, as_sel, bs_sel);
+        // refill the A buffer and the B buffer read at step kt - 1 between the two 64-K halves:
+        // the first half's fragment reads and MFMAs start right after the barrier
+        mma_step(a_lds, b_lds, as_sel, bs_sel, [&] {
+          if (next_a) {
+            issue_a(kt + 1);
+            load_scales(kt + 1, sa, sb);
+            // keep the scale loads ahead of the B loads: issued behind them they would be among
+            // the last DB loads, and the next step's wait would also wait for part of B(kt + 2)
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          if (next_b) issue_b(kt + 2, refill);
+        });
       };
       // A(kt), the scales of kt and B(kt) have landed before each step; B(kt + 1) may not have.
       // A single K step has a path of its own, so that the registers of the last step's scales
@@ -435,7 +440,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
         for (int t = 0; t < T::TM; ++t) as_sel[t] = (sc[wm * T::WTM + t * 32 + l32] >> (8 * g)) & 0x00FF00FFu;
 #pragma unroll
         for (int t = 0; t < T::TN; ++t) bs_sel[t] = (sc[BM + wn * T::WTN + t * 32 + l32] >> (8 * g)) & 0x00FF00FFu;
-        mma_step(a_lds, b_lds, as_sel, bs_sel);
+        mma_step(a_lds, b_lds, as_sel, bs_sel, [] {});
       }
     }  // main loop
 
