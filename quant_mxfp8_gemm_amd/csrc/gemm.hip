@@ -426,7 +426,12 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
         else
           wait_vm<0>();
         block_barrier();
-        if (kt + NS - 1 < KT) issue(kt + NS - 1, fill);  // refills the buffer read at step kt - 1
+        // refill the buffer read at step kt - 1: tiles of up to 128 rows issue the refill between
+        // the two 64-K halves (their first reads and MFMAs start at once; measured 2-3.5% faster),
+        // larger tiles right after the barrier (measured 1.5-4.5% faster that way)
+        constexpr bool kRefillMid = BM <= 128;
+        const int fill_now = fill;
+        if (!kRefillMid && kt + NS - 1 < KT) issue(kt + NS - 1, fill_now);
         fill = fill + 1 == NS ? 0 : fill + 1;
 
         const uint8_t* st = smem + buf * T::STAGE;
@@ -440,7 +445,9 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
         for (int t = 0; t < T::TM; ++t) as_sel[t] = (sc[wm * T::WTM + t * 32 + l32] >> (8 * g)) & 0x00FF00FFu;
 #pragma unroll
         for (int t = 0; t < T::TN; ++t) bs_sel[t] = (sc[BM + wn * T::WTN + t * 32 + l32] >> (8 * g)) & 0x00FF00FFu;
-        mma_step(a_lds, b_lds, as_sel, bs_sel, [] {});
+        mma_step(a_lds, b_lds, as_sel, bs_sel, [&] {
+          if (kRefillMid && kt + NS - 1 < KT) issue(kt + NS - 1, fill_now);
+        });
       }
     }  // main loop
 
