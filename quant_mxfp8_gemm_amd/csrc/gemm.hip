@@ -21,7 +21,9 @@
 //  * With swizzled, 16-byte aligned scales the 256 x 256 tile runs a split ring: A in two
 //    stage buffers and B in three (B fetched two steps ahead, all 160 KiB of LDS), the scales
 //    of a wave's rows loaded one step ahead into registers with one 8-byte and one 16-byte
-//    load (rows r, r+32, r+64, r+96 of a swizzled 128-row group are adjacent). Every other
+//    load (rows r, r+32, r+64, r+96 of a swizzled 128-row group are adjacent). Its refills,
+//    and those of the staged tiles of up to 128 rows, are issued between the two 64-K halves
+//    of a step, so the step's first fragment reads and MFMAs follow the barrier at once. Every other
 //    case uses NS-stage buffers holding A, B and the scale dwords together. Both give the same
 //    bits: every configuration sums the same MFMA partials in the same order.
 //  * The instruction applies the UE8M0 block scales itself. Operand layout (32 rows x 64 K):
