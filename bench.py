@@ -53,8 +53,8 @@ def _parse():
 # counter of a 1 GiB copy onto 1 GiB. Valid only for the kernel code it was taken on
 # (gemm_code_sha256).
 GEMM_TRAFFIC = {
-    "source_sha256": "6f8e9d7107ba68ce8fcc43b6b324f42c6a183d306a47001cc9d9adb326fc3127",
-    "fetch_kib": 456267.1, "write_kib": 393511.9,
+    "source_sha256": "d3f44de873e897833fff5cdb288a66dd167f745398d4300d5627359a413da329",
+    "fetch_kib": 456268.6, "write_kib": 393451.5,
     "fetch_factor": 2.0, "write_factor": 1.0,
 }
 

@@ -21,9 +21,10 @@
 //  * With swizzled, 16-byte aligned scales the 256 x 256 tile runs a split ring: A in two
 //    stage buffers and B in three (B fetched two steps ahead, all 160 KiB of LDS), the scales
 //    of a wave's rows loaded one step ahead into registers with one 8-byte and one 16-byte
-//    load (rows r, r+32, r+64, r+96 of a swizzled 128-row group are adjacent). Its refills,
-//    and those of the staged tiles of up to 128 rows, are issued between the two 64-K halves
-//    of a step, so the step's first fragment reads and MFMAs follow the barrier at once. Every other
+//    load (rows r, r+32, r+64, r+96 of a swizzled 128-row group are adjacent). Its A refill
+//    (and the refills of the staged tiles of up to 128 rows) is issued between the two 64-K
+//    halves of a step and its B refill after the step's MFMAs, so the step's first fragment
+//    reads and MFMAs follow the barrier at once. Every other
 //    case uses NS-stage buffers holding A, B and the scale dwords together. Both give the same
 //    bits: every configuration sums the same MFMA partials in the same order.
 //  * The instruction applies the UE8M0 block scales itself. Operand layout (32 rows x 64 K):
@@ -382,8 +383,9 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
         const uint8_t* a_lds = a_ring + (kt & 1) * T::A_BYTES;
         const uint8_t* b_lds = b_ring + bslot * T::B_BYTES;
         bslot = bslot == 2 ? 0 : bslot + 1;
-        // refill the A buffer and the B buffer read at step kt - 1 between the two 64-K halves:
-        // the first half's fragment reads and MFMAs start right after the barrier
+        // refill the A buffer read at step kt - 1 between the two 64-K halves (the first half's
+        // fragment reads and MFMAs start right after the barrier), and the B buffer read at step
+        // kt - 1 after the step's MFMAs (B is fetched two steps ahead, so it can wait)
         mma_step(a_lds, b_lds, as_sel, bs_sel, [&] {
           if (next_a) {
             issue_a(kt + 1);
@@ -392,8 +394,8 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
             // the last DB loads, and the next step's wait would also wait for part of B(kt + 2)
             __builtin_amdgcn_sched_barrier(0);
           }
-          if (next_b) issue_b(kt + 2, refill);
         });
+        if (next_b) issue_b(kt + 2, refill);
       };
       // A(kt), the scales of kt and B(kt) have landed before each step; B(kt + 1) may not have.
       // A single K step has a path of its own, so that the registers of the last step's scales
