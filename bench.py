@@ -53,8 +53,8 @@ def _parse():
 # counter of a 1 GiB copy onto 1 GiB. Valid only for the kernel code it was taken on
 # (gemm_code_sha256).
 GEMM_TRAFFIC = {
-    "source_sha256": "d3f44de873e897833fff5cdb288a66dd167f745398d4300d5627359a413da329",
-    "fetch_kib": 456268.6, "write_kib": 393451.5,
+    "source_sha256": "4bb40c0d13ace223d581984cf10b6c7707339660f0603c1404f5b2253c8f8e48",
+    "fetch_kib": 456266.7, "write_kib": 393485.2,
     "fetch_factor": 2.0, "write_factor": 1.0,
 }
 

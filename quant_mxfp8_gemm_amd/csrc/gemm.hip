@@ -458,7 +458,10 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
     if (EPI == EPI_SWIGLU) {
       // ---- fused epilogue: fp32 gate and up staged in LDS a band of rows at a time, then one
       // (row, 32-block of j) per thread: y = SiLU(g) * u, UE8M0 scale from amax, E4M3 codes
-      constexpr int SROW = BN * 4 + 16;  // bytes per staged row (gate floats, then up floats)
+      // Bytes per staged row (gate floats, then up floats). A staged column c sits at
+      // c ^ 16 where bit 6 of c is set: the readers below take 16 rows x 4 blocks of 32 columns
+      // at a time, and without it blocks b and b + 2 of a row would share their banks.
+      constexpr int SROW = BN * 4 + 16;
       constexpr int FIT = T::LDS_BYTES / SROW / 32 * 32;
       constexpr int PR = FIT < BM ? FIT : BM;  // rows per band
       static_assert(PR >= 32 && BM % PR == 0 && T::WTM % 32 == 0, "fused epilogue bands");
@@ -478,7 +481,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const int c = wn * T::WTN + x * 32 + 8 * q + 4 * g;
-              *(float4*)(smem + r * SROW + c * 4) =
+              *(float4*)(smem + r * SROW + (c ^ (((c >> 6) & 1) << 4)) * 4) =
                   make_float4(acc[x][y][4 * q + 0], acc[x][y][4 * q + 1], acc[x][y][4 * q + 2], acc[x][y][4 * q + 3]);
             }
         }
@@ -490,12 +493,13 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
           if (m >= m_end || j >= sg.inter) continue;
           const float* gp = (const float*)(smem + r * SROW) + 32 * b;
           const float* up = gp + HB;
+          const int xg = ((32 * b) & 64) >> 2, xu = ((32 * b + HB) & 64) >> 2;  // the column swizzle
           float yv[32];
           uint32_t amax = 0;
 #pragma unroll
           for (int e = 0; e < 32; e += 4) {
-            const float4 g4 = *(const float4*)(gp + e);
-            const float4 u4 = *(const float4*)(up + e);
+            const float4 g4 = *(const float4*)(gp + (e ^ xg));
+            const float4 u4 = *(const float4*)(up + (e ^ xu));
             const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
             const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
 #pragma unroll
@@ -521,16 +525,21 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
       continue;  // next tile (the fused output has no chunk counters)
     }
 
-    // ---- epilogue: BF16 tile staged in LDS, then full-line 16-byte stores
+    // ---- epilogue: BF16 tile staged in LDS, then full-line 16-byte stores. A staged row is
+    // 16 bytes longer than the tile row, so rows r and r + 8 (and r + 16) start in the same
+    // bank; each 8-byte write fills one half of a 16-byte group, and rows where bit 3 xor bit 4
+    // of r is set swap the halves of every group, so that the 32 rows of one write hit
+    // distinct banks (the readers swap them back).
     block_barrier();  // every wave is done reading the last stage
 #pragma unroll
     for (int x = 0; x < T::TN; ++x) {
 #pragma unroll
       for (int y = 0; y < T::TM; ++y) {
         const int r = wm * T::WTM + y * 32 + l32;
+        const int gs = g ^ (((r >> 3) ^ (r >> 4)) & 1);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int c = wn * T::WTN + x * 32 + 8 * q + 4 * g;
+          const int c = wn * T::WTN + x * 32 + 8 * q + 4 * gs;
           const uint32_t lo = pack_bf16x2(acc[x][y][4 * q + 0], acc[x][y][4 * q + 1]);
           const uint32_t hi = pack_bf16x2(acc[x][y][4 * q + 2], acc[x][y][4 * q + 3]);
           *(uint2*)(smem + r * T::C_STRIDE + c * 2) = make_uint2(lo, hi);
@@ -546,7 +555,8 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
       const int m = m0 + r;
       const int n = n0 + c8;
       if (m >= m_end || n >= N) continue;
-      const uint4 v = *(const uint4*)(smem + r * T::C_STRIDE + c8 * 2);
+      uint4 v = *(const uint4*)(smem + r * T::C_STRIDE + c8 * 2);
+      if (((r >> 3) ^ (r >> 4)) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
       uint16_t* dst = C + (int64_t)m * ldc + n;
       if (n + 8 <= N) {
         if (wide_store) {
