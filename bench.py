@@ -53,8 +53,8 @@ def _parse():
 # counter of a 1 GiB copy onto 1 GiB. Valid only for the kernel code it was taken on
 # (gemm_code_sha256).
 GEMM_TRAFFIC = {
-    "source_sha256": "4bb40c0d13ace223d581984cf10b6c7707339660f0603c1404f5b2253c8f8e48",
-    "fetch_kib": 456266.7, "write_kib": 393485.2,
+    "source_sha256": "b921e34ceae278f0c6c4501041123cddfee4cd30b7e857cefe97e7fd9d6ad53f",
+    "fetch_kib": 456269.6, "write_kib": 393502.2,
     "fetch_factor": 2.0, "write_factor": 1.0,
 }
 
@@ -280,7 +280,8 @@ def sweep(args, mx, synth, torch, dev):
         ts.sort()
         return ts[len(ts) // 2], ts[len(ts) // 10], ts[(9 * len(ts)) // 10]
 
-    shapes = [(128, 2048, mx.LINEAR, 1)] + [(m, 2048, mx.LINEAR, 4) for m in (512, 768, 1024, 1536, 2048, 4096)] \
+    shapes = [(32, 2048, mx.LINEAR, 1), (128, 2048, mx.LINEAR, 1)] \
+        + [(m, 2048, mx.LINEAR, 4) for m in (512, 768, 1024, 1536, 2048, 4096)] \
         + [(m, 3072, mx.SWIZZLED, 4) for m in (1024, 4096, 8192, 16384, 32768)] + [(32768, 2048, mx.SWIZZLED, 4)]
     wq = {}
     for k in (2048, 3072):

@@ -24,9 +24,11 @@
 //    load (rows r, r+32, r+64, r+96 of a swizzled 128-row group are adjacent). Its A refill
 //    (and the refills of the staged tiles of up to 128 rows) is issued between the two 64-K
 //    halves of a step and its B refill after the step's MFMAs, so the step's first fragment
-//    reads and MFMAs follow the barrier at once. Every other
-//    case uses NS-stage buffers holding A, B and the scale dwords together. Both give the same
-//    bits: every configuration sums the same MFMA partials in the same order.
+//    reads and MFMAs follow the barrier at once. With at most 32 rows in one chunk (decode)
+//    the BF16 GEMM uses one-wave 32 x 32 tiles whose fragments and scales go straight from memory
+//    into registers, four K steps ahead, with no LDS stages or barriers. Every other case uses
+//    NS-stage buffers holding A, B and the scale dwords together. All give the same bits:
+//    every configuration sums the same MFMA partials in the same order.
 //  * The instruction applies the UE8M0 block scales itself. Operand layout (32 rows x 64 K):
 //    lane l holds row l%32; with g = l/32, its bytes 0..15 are K 16g..16g+15 and bytes 16..31
 //    are K 32+16g..32+16g+15. The scale of (row r, 32-block b) comes from lane r + 32b, byte
@@ -64,12 +66,15 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int BK = 128;  // K bytes per stage
 constexpr int GM = 4;    // tile-rows per group
 
-template <int BM_, int BN_, int WMW, int WNW, int NS_, bool SPLIT_ = false>
+template <int BM_, int BN_, int WMW, int WNW, int NS_, bool SPLIT_ = false, bool DIRECT_ = false>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, NS = NS_;
   // SPLIT: A in a ring of two stage buffers and B in a ring of three (B is fetched two steps
   // ahead), the scales in registers; NS is not used
   static constexpr bool SPLIT = SPLIT_;
+  // DIRECT: no LDS stages; each wave loads its own MFMA fragments and scales from global
+  // memory into registers, NS steps ahead (LDS only stages the output tile)
+  static constexpr bool DIRECT = DIRECT_;
   static constexpr int NW = WMW * WNW, NT = NW * 64;
   static constexpr int WTM = BM / WMW, WTN = BN / WNW;  // wave sub-tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;    // MFMA blocks per wave
@@ -81,7 +86,7 @@ struct Tile {
   static constexpr int DS = (SROWS + 63) / 64;    // scale loads per wave per stage
   static constexpr int LOADS = DA + DB + DS;      // LDS-DMA instructions per wave per stage
   static constexpr int C_STRIDE = BN * 2 + 16;    // bytes per staged output row
-  static constexpr int RING_BYTES = SPLIT ? 2 * A_BYTES + 3 * B_BYTES : NS * STAGE;
+  static constexpr int RING_BYTES = SPLIT ? 2 * A_BYTES + 3 * B_BYTES : DIRECT ? 0 : NS * STAGE;
   static constexpr int LDS_BYTES = RING_BYTES > BM * C_STRIDE ? RING_BYTES : BM * C_STRIDE;
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "wave tile");
   static_assert(DA * NW * 1024 == A_BYTES && DB * NW * 1024 == B_BYTES, "data split");
@@ -416,6 +421,57 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
         step(KT - 1, false, false);
       }
 #endif
+    } else if constexpr (T::DIRECT) {
+      static_assert(T::TM == 1 && T::TN == 1 && EPI == EPI_BF16, "direct loads: one 32 x 32 block per wave");
+#if defined(__HIP_DEVICE_COMPILE__)
+      // Lane (l32, g) holds, for each 64-K half, the 16 bytes at K 16g and at K 32 + 16g of its
+      // A row and of its B row: the operand layout of the scaled MFMA, loaded as the LDS path
+      // reads it, so the products and their order are the same. Rows past the operand repeat
+      // its last row (their outputs are not stored).
+      constexpr int P = T::NS;  // steps in flight
+      const uint32_t arow = (uint32_t)min(m0 + wm * T::WTM + l32, M - 1);
+      const uint32_t brow = b_row(wn * T::WTN + l32);
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K);
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(B, (uint32_t)N * (uint32_t)K);
+      const uint32_t a_vo = arow * (uint32_t)K + 16 * g, b_vo = brow * (uint32_t)K + 16 * g;
+      const uint8_t* const sa_p = As + scale_base<A_LAYOUT>(arow, nblk4);
+      const uint8_t* const sb_p = Bs + scale_base<B_LAYOUT>(brow, nblk4);
+      v4i fa[P][4], fb[P][4];
+      uint32_t fsa[P], fsb[P];
+      // every load is issued unconditionally (steps past the end reload the last one), so the
+      // compiler's count of loads in flight is the same on every path
+      auto load = [&](int kt, int u) {
+        kt = min(kt, KT - 1);
+        const int k0 = kt * BK;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          fa[u][q] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, a_vo, k0 + 32 * q, 0));
+          fb[u][q] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rb, b_vo, k0 + 32 * q, 0));
+        }
+        fsa[u] = *(const uint32_t*)(sa_p + (uint32_t)kt * scale_step<A_LAYOUT>());
+        fsb[u] = *(const uint32_t*)(sb_p + (uint32_t)kt * scale_step<B_LAYOUT>());
+      };
+#pragma unroll
+      for (int u = 0; u < P; ++u) load(u, u);
+      for (int kt0 = 0; kt0 < KT; kt0 += P) {
+#pragma unroll
+        for (int u = 0; u < P; ++u) {
+          if (kt0 + u < KT) {
+            const int as_sel = (int)((fsa[u] >> (8 * g)) & 0x00FF00FFu);
+            const int bs_sel = (int)((fsb[u] >> (8 * g)) & 0x00FF00FFu);
+            const v4i* a4 = fa[u];
+            const v4i* b4 = fb[u];
+            const v8i a0 = {a4[0][0], a4[0][1], a4[0][2], a4[0][3], a4[1][0], a4[1][1], a4[1][2], a4[1][3]};
+            const v8i a1 = {a4[2][0], a4[2][1], a4[2][2], a4[2][3], a4[3][0], a4[3][1], a4[3][2], a4[3][3]};
+            const v8i b0 = {b4[0][0], b4[0][1], b4[0][2], b4[0][3], b4[1][0], b4[1][1], b4[1][2], b4[1][3]};
+            const v8i b1 = {b4[2][0], b4[2][1], b4[2][2], b4[2][3], b4[3][0], b4[3][1], b4[3][2], b4[3][3]};
+            acc[0][0] = mfma<0>(b0, a0, acc[0][0], bs_sel, as_sel);
+            acc[0][0] = mfma<2>(b1, a1, acc[0][0], bs_sel, as_sel);
+          }
+          load(kt0 + u + P, u);
+        }
+      }
+#endif
     } else {
       block_barrier();  // the previous tile's epilogue is done with LDS
 #pragma unroll
@@ -455,7 +511,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
       }
     }  // main loop
 
-    if (EPI == EPI_SWIGLU) {
+    if constexpr (EPI == EPI_SWIGLU) {
       // ---- fused epilogue: fp32 gate and up staged in LDS a band of rows at a time, then one
       // (row, 32-block of j) per thread: y = SiLU(g) * u, UE8M0 scale from amax, E4M3 codes
       // Bytes per staged row (gate floats, then up floats). A staged column c sits at
@@ -589,6 +645,7 @@ using TileR = Tile<96, 192, 3, 2, 4>;   // 6 waves of 32 x 96
 using TileM = Tile<128, 128, 4, 2, 4>;  // 8 waves of 32 x 64
 using TileS = Tile<64, 128, 2, 4, 4>;   // 8 waves of 32 x 32
 using TileT = Tile<32, 128, 1, 4, 4>;   // 4 waves of 32 x 32; a few rows per chunk
+using TileD = Tile<32, 32, 1, 1, 4, false, true>;  // one wave, fragments loaded to registers
 
 constexpr int REF_CUS = 256;  // compute units the tile choice is made for (MI355X)
 
@@ -608,7 +665,7 @@ int64_t tile_count(int64_t m, int64_t n, int num_chunks, int bm, int bn) {
   return (int64_t)num_chunks * ((m / num_chunks + bm - 1) / bm) * ((n + bn - 1) / bn);
 }
 
-enum { CFG_L, CFG_N, CFG_Q, CFG_W, CFG_R, CFG_M, CFG_S, CFG_T };
+enum { CFG_L, CFG_N, CFG_Q, CFG_W, CFG_R, CFG_M, CFG_S, CFG_T, CFG_D };
 
 // Tile choice by estimated makespan: rounds of workgroups over the compute units times the
 // time of one tile's 128-K step, measured per configuration on MI355X (N = 6144 sweeps, in
@@ -641,12 +698,27 @@ int pick_config(int64_t m, int64_t n, int num_chunks) {
   return best;
 }
 
+// The BF16-output GEMM of at most 32 rows in one chunk (decode sizes) takes one-wave 32 x 32
+// tiles that load their fragments straight into registers: four times the workgroups of the
+// 32 x 128 tile (whose N / 128 workgroups leave most CUs idle), each without LDS stages or
+// barriers (M = 1, 8 and 32 at K = 2048: 11.0, 11.3 and 12.5 us against 12.6, 13.0 and
+// 14.6). Once the 32 x 128 tile has more workgroups it is faster: its LDS-DMA loads cover
+// 8 rows x 128 bytes per instruction where a register load covers 32 rows x 32 bytes, and
+// the extra requests cost more than the barriers saved (M = 64: 16.8 against 14.1 us; M = 128
+// in four chunks of 32 rows: 20.9 against 12.1 us).
+int pick_config_bf16(int64_t m, int64_t n, int num_chunks) {
+  const int c = pick_config(m, n, num_chunks);
+  return c == CFG_T && num_chunks == 1 && m <= 32 ? CFG_D : c;
+}
+
 template <class T, int EPI = EPI_BF16>
 hipError_t launch_cfg(const uint8_t* a, const uint8_t* as, int a_layout, const uint8_t* b, const uint8_t* bs,
                       int b_layout, int64_t m, int64_t n, int64_t k, uint16_t* c, int64_t ldc, int num_chunks,
                       int first_chunk, int* chunk_done, hipStream_t stream, SwiGluOut sg = SwiGluOut{}) {
   const int64_t tiles = tile_count(m, n, num_chunks, T::BM, T::BN);
-  const int64_t grid = tiles < device_cu_count() ? tiles : device_cu_count();
+  // one-wave direct tiles: up to eight workgroups per compute unit; the others: one
+  const int64_t cap = (T::DIRECT ? 8 : 1) * (int64_t)device_cu_count();
+  const int64_t grid = tiles < cap ? tiles : cap;
   const int wide = ((uintptr_t)c % 16 == 0 && ldc % 8 == 0) ? 1 : 0;
   const dim3 g((unsigned)grid), blk(T::NT);
   const int M = (int)m, N = (int)n, K = (int)k, L = (int)ldc;
@@ -684,7 +756,7 @@ hipError_t launch_split(const uint8_t* a, const uint8_t* as, const uint8_t* b, c
 }  // namespace
 
 GemmShape gemm_pick_shape(int64_t m, int64_t n, int num_chunks) {
-  switch (pick_config(m, n, num_chunks)) {
+  switch (pick_config_bf16(m, n, num_chunks)) {
     case CFG_L: return GemmShape{TileL::BM, TileL::BN};
     case CFG_N: return GemmShape{TileN::BM, TileN::BN};
     case CFG_Q: return GemmShape{TileQ::BM, TileQ::BN};
@@ -692,6 +764,7 @@ GemmShape gemm_pick_shape(int64_t m, int64_t n, int num_chunks) {
     case CFG_W: return GemmShape{TileW::BM, TileW::BN};
     case CFG_M: return GemmShape{TileM::BM, TileM::BN};
     case CFG_S: return GemmShape{TileS::BM, TileS::BN};
+    case CFG_D: return GemmShape{TileD::BM, TileD::BN};
     default: return GemmShape{TileT::BM, TileT::BN};
   }
 }
@@ -725,7 +798,7 @@ hipError_t launch_gemm_silu_mul_quant(const uint8_t* a, const uint8_t* as, int a
 hipError_t launch_gemm(const uint8_t* a, const uint8_t* as, int a_layout, const uint8_t* b,
                        const uint8_t* bs, int b_layout, int64_t m, int64_t n, int64_t k, uint16_t* c,
                        int64_t ldc, int num_chunks, int first_chunk, int* chunk_done, hipStream_t stream) {
-  switch (pick_config(m, n, num_chunks)) {
+  switch (pick_config_bf16(m, n, num_chunks)) {
     case CFG_L:
       if (split_ring_fits(as, a_layout, bs, b_layout, m, num_chunks))
         return launch_split<EPI_BF16>(a, as, b, bs, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
@@ -742,6 +815,8 @@ hipError_t launch_gemm(const uint8_t* a, const uint8_t* as, int a_layout, const 
       return launch_cfg<TileM>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
     case CFG_S:
       return launch_cfg<TileS>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
+    case CFG_D:
+      return launch_cfg<TileD>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
     default:
       return launch_cfg<TileT>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
   }

@@ -176,6 +176,12 @@ def test_tiles_per_chunk(lib):
     assert mx.gemm_tiles_per_chunk(32768, 6144, 4) == 32 * 24    # 256 x 256
     assert mx.gemm_tiles_per_chunk(1024, 6144, 4) == 2 * 32      # 128 x 192: one full round
     assert mx.gemm_tiles_per_chunk(512, 6144, 4) == 1 * 48       # 128 x 128
+    assert mx.gemm_tiles_per_chunk(128, 6144, 1) == 4 * 48       # 32 x 128
+    assert mx.gemm_tiles_per_chunk(128, 6144, 4) == 1 * 48       # 32 x 128
+    assert mx.gemm_tiles_per_chunk(33, 6144, 1) == 2 * 48
+    assert mx.gemm_tiles_per_chunk(32, 6144, 1) == 192           # 32 x 32, register-loaded
+    assert mx.gemm_tiles_per_chunk(1, 6144, 1) == 192
+    assert mx.gemm_tiles_per_chunk(32, 6144, 2) == 48            # 32 x 128 (two chunks)
     assert mx.gemm_tiles_per_chunk(4096, 6144, 4) == 4 * 32      # 256 x 192: two full rounds
     assert mx.gemm_tiles_per_chunk(3072, 6144, 4) == 4 * 32      # 192 x 192: 768 rows per chunk, no empty rows
     assert mx.gemm_tiles_per_chunk(3000, 6144, 4) == 4 * 32      # 192 x 192 (256 x 192 would give 3 x 32)

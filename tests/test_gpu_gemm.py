@@ -106,7 +106,8 @@ def test_gemm_small_full(m, n, k, chunks, la, lb):
 TILE_CASES = [(2000, 8000, 256, 1, 256, 256), (1000, 12200, 256, 1, 256, 192), (3000, 6100, 256, 4, 192, 192),
               (1016, 6100, 256, 4, 128, 192), (760, 6100, 256, 4, 96, 192),
               (200, 12250, 256, 1, 128, 128),
-              (100, 12200, 256, 1, 64, 128), (132, 6100, 256, 4, 32, 128)]
+              (100, 12200, 256, 1, 64, 128), (132, 6100, 256, 4, 32, 128),
+              (30, 6100, 640, 1, 32, 32), (17, 6100, 384, 1, 32, 32)]
 
 
 @pytest.mark.parametrize("la,lb", [(0, 1), (1, 0)])
@@ -231,8 +232,8 @@ def test_gemm_edge_shapes_full(m, n, k, chunks):
 
 
 def test_gemm_chunk_counters_small_tiles():
-    """chunk_done with the smallest tiles (32 rows per chunk): every chunk counts all its tiles
-    and the output does not depend on the chunking."""
+    """chunk_done with the smallest LDS tiles (32 rows per chunk): every chunk counts all its
+    tiles and the output does not depend on the chunking."""
     m, n, k = 128, 6144, 512
     qa, sa, qb, sb = _operands(m, n, k)
     c1 = _gpu_gemm(qa, sa[0], 0, qb, sb[0], 0, num_chunks=1)
@@ -240,6 +241,22 @@ def test_gemm_chunk_counters_small_tiles():
     c4 = _gpu_gemm(qa, sa[0], 0, qb, sb[0], 0, num_chunks=4, first_chunk=3, chunk_done=done)
     assert np.array_equal(c1, c4)
     assert done.cpu().tolist() == [mx.gemm_tiles_per_chunk(m, n, 4)] * 4 == [48] * 4
+
+
+def test_gemm_direct_tiles_count_and_match():
+    """At most 32 rows in one chunk take one-wave 32 x 32 tiles with register-loaded fragments:
+    chunk_done counts every one of them, and the output equals the oracle's and, bit for bit,
+    that of the 32 x 128 LDS tile (the same rows as one chunk of a taller problem)."""
+    m, n, k = 20, 6144, 640
+    qa, sa, qb, sb = _operands(m + 108, n, k, seed_a=21, seed_b=22)
+    done = torch.zeros(1, dtype=torch.int32, device="cuda")
+    c = _gpu_gemm(qa[:m], sa[0][:m], 0, qb, sb[0], 0, num_chunks=1, chunk_done=done)
+    assert done.cpu().tolist() == [mx.gemm_tiles_per_chunk(m, n, 1)] == [192]
+    ref = oracle.gemm(qa[:m], sa[0][:m], 0, qb, sb[0], 0)
+    _assert_close(c, ref, _abs_sum_full(qa[:m], sa[0][:m], 0, qb, sb[0], 0), "direct tiles m=20")
+    assert mx.gemm_tiles_per_chunk(m + 108, n, 1) == 4 * 48
+    c_lds = _gpu_gemm(qa, sa[0], 0, qb, sb[0], 0, num_chunks=1)
+    assert np.array_equal(c, c_lds[:m])
 
 
 def test_gemm_chunking_is_bitwise_invariant():
