@@ -107,7 +107,7 @@ TILE_CASES = [(2000, 8000, 256, 1, 256, 256), (1000, 12200, 256, 1, 256, 192), (
               (1016, 6100, 256, 4, 128, 192), (760, 6100, 256, 4, 96, 192),
               (200, 12250, 256, 1, 128, 128),
               (100, 12200, 256, 1, 64, 128), (132, 6100, 256, 4, 32, 128),
-              (30, 6100, 640, 1, 32, 32), (17, 6100, 384, 1, 32, 32)]
+              (30, 6100, 640, 1, 32, 32), (17, 6100, 384, 1, 32, 32), (5, 1000, 128, 1, 32, 32)]
 
 
 @pytest.mark.parametrize("la,lb", [(0, 1), (1, 0)])
