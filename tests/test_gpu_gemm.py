@@ -357,3 +357,31 @@ def test_gemm_wide_scale_range_split_ring():
     ref, exact = oracle.gemm_sampled(qa, sa[1], 1, qb, sb[1], 1, ri, ci)
     _assert_mass_bound(c[ri, ci], ref, exact, _abs_sum_sampled(qa, sa[1], 1, qb, sb[1], 1, ri, ci),
                        "wide scales split ring")
+
+
+def _random_case(seed):
+    """A GEMM shape drawn from a seeded generator: M from 1 to 3000 (decode to mid-size), N up
+    to 6400 with a ragged tail, K from 128 to 1408, 1, 2 or 4 chunks, either scale layout on
+    either side; the tile is whatever the library picks for it."""
+    rng = np.random.default_rng(seed)
+    m = int(rng.choice([rng.integers(1, 33), rng.integers(33, 300), rng.integers(300, 3000)]))
+    n = int(rng.integers(1, 200)) * 32 + int(rng.integers(0, 32))
+    k = int(rng.integers(1, 12)) * 128
+    chunks = int(rng.choice([1, 2, 4]))
+    m = max(chunks, m // chunks * chunks)
+    return m, n, k, chunks, int(rng.integers(0, 2)), int(rng.integers(0, 2)), int(rng.integers(0, chunks))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_gemm_random_shapes_mass_bound(seed):
+    """Random shapes in full against the oracle, held to the accumulation bound: every output
+    within 4e-5 of its dot product's absolute mass plus one BF16 ulp of the exact sum (a fixed
+    relative bar does not hold for arbitrary shapes, where an output that cancels to a thousandth
+    of its mass carries the same absolute accumulation error)."""
+    m, n, k, chunks, la, lb, first = _random_case(1000 + seed)
+    print(f"gemm random seed={seed}: m={m} n={n} k={k} chunks={chunks} layouts={la}{lb} "
+          f"tiles/chunk={mx.gemm_tiles_per_chunk(m, n, chunks)}", flush=True)
+    qa, sa, qb, sb = _operands(m, n, k, seed_a=3000 + seed, seed_b=4000 + seed)
+    ref, exact = oracle.gemm(qa, sa[la], la, qb, sb[lb], lb, want_f64=True)
+    c = _gpu_gemm(qa, sa[la], la, qb, sb[lb], lb, num_chunks=chunks, first_chunk=first)
+    _assert_mass_bound(c, ref, exact, _abs_sum_full(qa, sa[la], la, qb, sb[lb], lb), f"random seed={seed}")
