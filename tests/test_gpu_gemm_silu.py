@@ -146,3 +146,19 @@ def test_gemm_silu_mul_quant_feeds_down_proj():
     c2 = mx.gemm(q, s_lin, mx.LINEAR, wd, wds, mx.SWIZZLED, num_chunks=4)
     torch.cuda.synchronize()
     assert torch.equal(c1.view(torch.int16), c2.view(torch.int16))
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_gemm_silu_mul_quant_random_shapes(seed):
+    """Seeded random shapes (M 1-1500, inter a multiple of 32 up to 1888, K 128-896, either scale
+    layout on either side) in full, with the same decision bounds as the fixed cases."""
+    rng = np.random.default_rng(5000 + seed)
+    m, inter, k = int(rng.integers(1, 1500)), int(rng.integers(1, 60)) * 32, int(rng.integers(1, 8)) * 128
+    la, lw = int(rng.integers(0, 2)), int(rng.integers(0, 2))
+    print(f"gemm_silu_mul_quant random seed={seed}: m={m} inter={inter} k={k} layouts={la}{lw}", flush=True)
+    qa, sa, qw, sw = _operands(m, inter, k, seed_a=6000 + seed, seed_w=7000 + seed)
+    q, s_lin, s_swz = _run(qa, sa[la], la, qw, sw[lw], lw)
+    q_ref, s_ref, _, gu = oracle.gemm_silu_mul_quant(qa, sa[la], la, qw, sw[lw], lw, want_gu=True)
+    s_diff, v_diff = silu_mul_quant_check(q, s_lin, gu, _mass(qa, sa[la], la, qw, sw[lw], lw, range(m)), inter)
+    assert s_diff <= 0.01 and v_diff <= 0.01
+    assert np.array_equal(s_swz, oracle.swizzle_scales(s_lin))
