@@ -53,8 +53,8 @@ def _parse():
 # counter of a 1 GiB copy onto 1 GiB. Valid only for the kernel code it was taken on
 # (gemm_code_sha256).
 GEMM_TRAFFIC = {
-    "source_sha256": "b921e34ceae278f0c6c4501041123cddfee4cd30b7e857cefe97e7fd9d6ad53f",
-    "fetch_kib": 456269.6, "write_kib": 393502.2,
+    "source_sha256": "5f8c7f1e095d0d1c66ad08900020b3929041501a6ea1efa762e77f777ee75e21",
+    "fetch_kib": 456277.9, "write_kib": 393365.3,
     "fetch_factor": 2.0, "write_factor": 1.0,
 }
 

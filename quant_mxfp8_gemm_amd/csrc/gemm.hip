@@ -26,7 +26,7 @@
 //    halves of a step and its B refill after the step's MFMAs, so the step's first fragment
 //    reads and MFMAs follow the barrier at once. With at most 32 rows in one chunk (decode)
 //    the BF16 GEMM uses one-wave 32 x 32 tiles whose fragments and scales go straight from memory
-//    into registers, four K steps ahead, with no LDS stages or barriers. Every other case uses
+//    into registers, eight K steps ahead, with no LDS stages or barriers. Every other case uses
 //    NS-stage buffers holding A, B and the scale dwords together. All give the same bits:
 //    every configuration sums the same MFMA partials in the same order.
 //  * The instruction applies the UE8M0 block scales itself. Operand layout (32 rows x 64 K):
@@ -645,7 +645,7 @@ using TileR = Tile<96, 192, 3, 2, 4>;   // 6 waves of 32 x 96
 using TileM = Tile<128, 128, 4, 2, 4>;  // 8 waves of 32 x 64
 using TileS = Tile<64, 128, 2, 4, 4>;   // 8 waves of 32 x 32
 using TileT = Tile<32, 128, 1, 4, 4>;   // 4 waves of 32 x 32; a few rows per chunk
-using TileD = Tile<32, 32, 1, 1, 4, false, true>;  // one wave, fragments loaded to registers
+using TileD = Tile<32, 32, 1, 1, 8, false, true>;  // one wave, fragments loaded to registers
 
 constexpr int REF_CUS = 256;  // compute units the tile choice is made for (MI355X)
 
@@ -701,7 +701,7 @@ int pick_config(int64_t m, int64_t n, int num_chunks) {
 // The BF16-output GEMM of at most 32 rows in one chunk (decode sizes) takes one-wave 32 x 32
 // tiles that load their fragments straight into registers: four times the workgroups of the
 // 32 x 128 tile (whose N / 128 workgroups leave most CUs idle), each without LDS stages or
-// barriers (M = 1, 8 and 32 at K = 2048: 11.0, 11.3 and 12.5 us against 12.6, 13.0 and
+// barriers (M = 1, 8 and 32 at K = 2048: 9.9, 10.6 and 12.7 us against 12.6, 13.0 and
 // 14.6). Once the 32 x 128 tile has more workgroups it is faster: its LDS-DMA loads cover
 // 8 rows x 128 bytes per instruction where a register load covers 32 rows x 32 bytes, and
 // the extra requests cost more than the barriers saved (M = 64: 16.8 against 14.1 us; M = 128
