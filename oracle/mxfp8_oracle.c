@@ -38,7 +38,7 @@
  *    2^(sa[m,kb]-127) * 2^(sb[n,kb]-127) * sum_{i<32} A[m,32kb+i] * B[n,32kb+i],
  *    rounded once to BF16 (round to nearest even). A is [M,K] and B is [N,K],
  *    both K-contiguous.
- *  - The fused dense GEMM1 (PR #65496 "Details", PR #64111 "Claims"): with the
+ *  - The fused dense GEMM1 (PR #64659 "Details", PR #64111 "Claims"): with the
  *    merged gate_up weight (gate rows, then up rows), y = SiLU(g) * u where
  *    SiLU(g) = g / (1 + e^-g), g and u exact GEMM values, y in fp64 rounded once
  *    to fp32 and quantised like the norm output.
@@ -441,9 +441,10 @@ int oracle_mxfp8_gemm_sampled(const uint8_t* a, const uint8_t* as, int a_layout,
 
 /*
  * The dense MLP's first GEMM with its activation and quantisation fused, producing the MXFP8
- * activation down_proj consumes (vLLM PR #65496, "Details: GEMM-RS with a quantized input":
- * above the token threshold the fused dense GEMM1 hands down_proj an MXFP8 QuantizedActivation
- * with swizzled scales). w: E4M3 [2*inter, k], rows [0, inter) the gate projection and rows
+ * activation down_proj consumes. vLLM PR #64659 ("Details", "GEMM-RS with a quantized input")
+ * states that past its token threshold this GEMM emits MXFP8 data with scales already in the
+ * swizzled layout, which the GEMM-RS path then uses without quantising again; PR #64111
+ * ("Claims") lists the fused dense GEMM1 among its decode kernels. w: E4M3 [2*inter, k], rows [0, inter) the gate projection and rows
  * [inter, 2*inter) the up projection. For each listed row r of a and each j < inter:
  *   g = C[r, j], u = C[r, inter + j]          (exact values, as gemm_element above)
  *   y = g / (1 + e^-g) * u                    (SiLU(g) times up, in fp64)

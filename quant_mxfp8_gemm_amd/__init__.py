@@ -101,6 +101,45 @@ def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
+def _same_device(ref: torch.Tensor, **tensors):
+    """Every tensor (None skipped) is a GPU tensor on ref's device."""
+    _dev(ref, "input")
+    for name, t in tensors.items():
+        if t is not None and _dev(t, name).device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, the inputs on {ref.device}")
+
+
+def _u8_buffer(t, name: str, numel: int = None, shape=None):
+    """A contiguous uint8 tensor of the given shape, or of at least numel bytes. The library
+    cannot see buffer sizes, so an undersized buffer is rejected here rather than becoming an
+    out-of-bounds device access."""
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous uint8 tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} bytes, {numel} are needed")
+    return t
+
+
+def _quant_outputs(out, rows: int, k: int, linear: bool, swizzled: bool, like: torch.Tensor):
+    """Checked caller-provided (q, scales_linear, scales_swizzled), or new ones on like's device."""
+    if out is None:
+        q = torch.empty((rows, k), dtype=torch.uint8, device=like.device)
+        s_lin = torch.empty((rows, k // 32), dtype=torch.uint8, device=like.device) if linear else None
+        s_swz = torch.empty(scale_bytes(rows, k, SWIZZLED), dtype=torch.uint8, device=like.device) if swizzled else None
+        return q, s_lin, s_swz
+    q, s_lin, s_swz = out
+    _u8_buffer(q, "q", shape=(rows, k))
+    if s_lin is not None:
+        _u8_buffer(s_lin, "scales_linear", shape=(rows, k // 32))
+    if s_swz is not None:
+        _u8_buffer(s_swz, "scales_swizzled", numel=scale_bytes(rows, k, SWIZZLED))
+    if s_lin is None and s_swz is None:
+        raise ValueError("at least one scale layout must be requested")
+    return q, s_lin, s_swz
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -110,8 +149,7 @@ def _stream(t: torch.Tensor):
 
 
 def _rows_view(x: torch.Tensor, name: str, dtype):
-    _dev(x, name)
-    if x.dtype != dtype or x.dim() != 2 or x.stride(1) != 1:
+    if not isinstance(x, torch.Tensor) or x.dtype != dtype or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError(f"{name} must be a 2-D {dtype} tensor with unit column stride")
     return x
 
@@ -123,12 +161,10 @@ def quantize(x: torch.Tensor, linear: bool = True, swizzled: bool = True, out=No
     """
     _rows_view(x, "x", torch.bfloat16)
     rows, k = x.shape
-    if out is not None:
-        q, s_lin, s_swz = out
-    else:
-        q = torch.empty((rows, k), dtype=torch.uint8, device=x.device)
-        s_lin = torch.empty((rows, k // 32), dtype=torch.uint8, device=x.device) if linear else None
-        s_swz = torch.empty(scale_bytes(rows, k, SWIZZLED), dtype=torch.uint8, device=x.device) if swizzled else None
+    if k % 32 != 0:
+        raise ValueError("k must be a multiple of 32")
+    q, s_lin, s_swz = _quant_outputs(out, rows, k, linear, swizzled, x)
+    _same_device(x, q=q, scales_linear=s_lin, scales_swizzled=s_swz)
     st = load_library().mxfp8_quantize(_ptr(x), rows, k, x.stride(0), _ptr(q), _ptr(s_lin), _ptr(s_swz), _stream(x))
     if st != OK:
         raise MXFP8Error("mxfp8_quantize", st)
@@ -142,16 +178,13 @@ def rmsnorm_quant(x: torch.Tensor, w: torch.Tensor, eps: float = 1e-6, linear: b
     Returns ``(q [rows, hidden] u8, scales_linear, scales_swizzled)``.
     """
     _rows_view(x, "x", torch.bfloat16)
-    _dev(w, "w")
     rows, h = x.shape
-    if w.dtype != torch.bfloat16 or w.shape != (h,) or not w.is_contiguous():
+    if h % 32 != 0:
+        raise ValueError("hidden must be a multiple of 32")
+    if not isinstance(w, torch.Tensor) or w.dtype != torch.bfloat16 or tuple(w.shape) != (h,) or not w.is_contiguous():
         raise ValueError("w must be a contiguous bfloat16 [hidden] tensor")
-    if out is not None:
-        q, s_lin, s_swz = out
-    else:
-        q = torch.empty((rows, h), dtype=torch.uint8, device=x.device)
-        s_lin = torch.empty((rows, h // 32), dtype=torch.uint8, device=x.device) if linear else None
-        s_swz = torch.empty(scale_bytes(rows, h, SWIZZLED), dtype=torch.uint8, device=x.device) if swizzled else None
+    q, s_lin, s_swz = _quant_outputs(out, rows, h, linear, swizzled, x)
+    _same_device(x, w=w, q=q, scales_linear=s_lin, scales_swizzled=s_swz)
     st = load_library().rmsnorm_quant_mxfp8(_ptr(x), _ptr(w), rows, h, x.stride(0), float(eps), _ptr(q),
                                             _ptr(s_lin), _ptr(s_swz), _stream(x))
     if st != OK:
@@ -166,18 +199,15 @@ def add_rmsnorm_quant(x: torch.Tensor, residual: torch.Tensor, w: torch.Tensor, 
     scales_swizzled)``."""
     _rows_view(x, "x", torch.bfloat16)
     _rows_view(residual, "residual", torch.bfloat16)
-    _dev(w, "w")
     rows, h = x.shape
+    if h % 32 != 0:
+        raise ValueError("hidden must be a multiple of 32")
     if residual.shape != x.shape:
         raise ValueError("residual must have the shape of x")
-    if w.dtype != torch.bfloat16 or w.shape != (h,) or not w.is_contiguous():
+    if not isinstance(w, torch.Tensor) or w.dtype != torch.bfloat16 or tuple(w.shape) != (h,) or not w.is_contiguous():
         raise ValueError("w must be a contiguous bfloat16 [hidden] tensor")
-    if out is not None:
-        q, s_lin, s_swz = out
-    else:
-        q = torch.empty((rows, h), dtype=torch.uint8, device=x.device)
-        s_lin = torch.empty((rows, h // 32), dtype=torch.uint8, device=x.device) if linear else None
-        s_swz = torch.empty(scale_bytes(rows, h, SWIZZLED), dtype=torch.uint8, device=x.device) if swizzled else None
+    q, s_lin, s_swz = _quant_outputs(out, rows, h, linear, swizzled, x)
+    _same_device(x, residual=residual, w=w, q=q, scales_linear=s_lin, scales_swizzled=s_swz)
     st = load_library().add_rmsnorm_quant_mxfp8(_ptr(x), _ptr(residual), _ptr(w), rows, h, x.stride(0),
                                                 residual.stride(0), float(eps), _ptr(q), _ptr(s_lin), _ptr(s_swz),
                                                 _stream(x))
@@ -189,18 +219,17 @@ def add_rmsnorm_quant(x: torch.Tensor, residual: torch.Tensor, w: torch.Tensor, 
 def swizzle_scales(scales_linear: torch.Tensor, k: int = None, out: torch.Tensor = None) -> torch.Tensor:
     """Linear UE8M0 scales ``[rows, k/32]`` u8 -> the flat 128x4-swizzled buffer (pad bytes 0),
     the step after gathering MXFP8 activations by rows. ``k`` defaults to 32 x the column count."""
-    _dev(scales_linear, "scales_linear")
-    if scales_linear.dtype != torch.uint8 or scales_linear.dim() != 2 or not scales_linear.is_contiguous():
+    if not isinstance(scales_linear, torch.Tensor) or scales_linear.dim() != 2:
         raise ValueError("scales_linear must be a contiguous 2-D uint8 tensor")
+    _u8_buffer(scales_linear, "scales_linear")
     rows, nblk = scales_linear.shape
     k = 32 * nblk if k is None else int(k)
-    if k != 32 * nblk:
+    if k != 32 * nblk or nblk == 0:
         raise ValueError("k must be 32 x the number of scale columns")
     if out is None:
         out = torch.empty(scale_bytes(rows, k, SWIZZLED), dtype=torch.uint8, device=scales_linear.device)
-    _dev(out, "out")
-    if out.dtype != torch.uint8 or not out.is_contiguous() or out.numel() < scale_bytes(rows, k, SWIZZLED):
-        raise ValueError("out must be a contiguous uint8 tensor of scale_bytes(rows, k, SWIZZLED) bytes")
+    _u8_buffer(out, "out", numel=scale_bytes(rows, k, SWIZZLED))
+    _same_device(scales_linear, out=out)
     st = load_library().mxfp8_swizzle_scales(_ptr(scales_linear), rows, k, _ptr(out), _stream(scales_linear))
     if st != OK:
         raise MXFP8Error("mxfp8_swizzle_scales", st)
@@ -217,14 +246,16 @@ def gemm(a: torch.Tensor, a_scales: torch.Tensor, a_layout: int, b: torch.Tensor
     produced as ``num_chunks`` row chunks starting with ``first_chunk``; ``chunk_done`` (int32
     ``[num_chunks]``, zeroed by the caller) counts finished tiles per chunk.
     """
-    for t, nm in ((a, "a"), (b, "b"), (a_scales, "a_scales"), (b_scales, "b_scales")):
-        _dev(t, nm)
-        if t.dtype != torch.uint8 or not t.is_contiguous():
-            raise ValueError(f"{nm} must be a contiguous uint8 tensor")
+    for t, nm in ((a, "a"), (b, "b")):
+        _u8_buffer(t, nm)
     if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[1]:
         raise ValueError("a must be [m, k] and b [n, k]")
     m, k = a.shape
     n = b.shape[0]
+    if k % 32 != 0 or int(a_layout) not in (LINEAR, SWIZZLED) or int(b_layout) not in (LINEAR, SWIZZLED):
+        raise ValueError("k must be a multiple of 32 and the scale layouts LINEAR or SWIZZLED")
+    _u8_buffer(a_scales, "a_scales", numel=scale_bytes(m, k, a_layout))
+    _u8_buffer(b_scales, "b_scales", numel=scale_bytes(n, k, b_layout))
     if out is None:
         ldc = (n + 3) // 4 * 4  # the kernels store 4 columns at a time: keep rows 8-byte aligned
         out = torch.empty((m, ldc), dtype=torch.bfloat16, device=a.device)[:, :n]
@@ -232,9 +263,10 @@ def gemm(a: torch.Tensor, a_scales: torch.Tensor, a_layout: int, b: torch.Tensor
     if out.shape[0] != m or out.shape[1] < n:
         raise ValueError("out must be [m, >=n]")
     if chunk_done is not None:
-        _dev(chunk_done, "chunk_done")
-        if chunk_done.dtype != torch.int32 or chunk_done.numel() < num_chunks or not chunk_done.is_contiguous():
+        if not isinstance(chunk_done, torch.Tensor) or chunk_done.dtype != torch.int32 or \
+                chunk_done.numel() < num_chunks or not chunk_done.is_contiguous():
             raise ValueError("chunk_done must be a contiguous int32 tensor with num_chunks entries")
+    _same_device(a, b=b, a_scales=a_scales, b_scales=b_scales, out=out, chunk_done=chunk_done)
     st = load_library().mxfp8_gemm_bf16out(_ptr(a), _ptr(a_scales), int(a_layout), _ptr(b), _ptr(b_scales),
                                            int(b_layout), m, n, k, _ptr(out), out.stride(0), int(num_chunks),
                                            int(first_chunk), _ptr(chunk_done), _stream(a))
@@ -252,20 +284,19 @@ def gemm_silu_mul_quant(a: torch.Tensor, a_scales: torch.Tensor, a_layout: int, 
     contiguous, scales in the given layouts. Returns ``(q [m, inter] u8, scales_linear,
     scales_swizzled)``; ``out`` may pass them preallocated.
     """
-    for t, nm in ((a, "a"), (w, "w"), (a_scales, "a_scales"), (w_scales, "w_scales")):
-        _dev(t, nm)
-        if t.dtype != torch.uint8 or not t.is_contiguous():
-            raise ValueError(f"{nm} must be a contiguous uint8 tensor")
+    for t, nm in ((a, "a"), (w, "w")):
+        _u8_buffer(t, nm)
     if a.dim() != 2 or w.dim() != 2 or a.shape[1] != w.shape[1] or w.shape[0] % 2 != 0:
         raise ValueError("a must be [m, k] and w [2*inter, k]")
     m, k = a.shape
     inter = w.shape[0] // 2
-    if out is not None:
-        q, s_lin, s_swz = out
-    else:
-        q = torch.empty((m, inter), dtype=torch.uint8, device=a.device)
-        s_lin = torch.empty((m, inter // 32), dtype=torch.uint8, device=a.device) if linear else None
-        s_swz = torch.empty(scale_bytes(m, inter, SWIZZLED), dtype=torch.uint8, device=a.device) if swizzled else None
+    if k % 32 != 0 or inter % 32 != 0 or int(a_layout) not in (LINEAR, SWIZZLED) or \
+            int(w_layout) not in (LINEAR, SWIZZLED):
+        raise ValueError("k and inter must be multiples of 32 and the scale layouts LINEAR or SWIZZLED")
+    _u8_buffer(a_scales, "a_scales", numel=scale_bytes(m, k, a_layout))
+    _u8_buffer(w_scales, "w_scales", numel=scale_bytes(2 * inter, k, w_layout))
+    q, s_lin, s_swz = _quant_outputs(out, m, inter, linear, swizzled, a)
+    _same_device(a, w=w, a_scales=a_scales, w_scales=w_scales, q=q, scales_linear=s_lin, scales_swizzled=s_swz)
     st = load_library().mxfp8_gemm_silu_mul_quant(_ptr(a), _ptr(a_scales), int(a_layout), _ptr(w), _ptr(w_scales),
                                                   int(w_layout), m, inter, k, _ptr(q), _ptr(s_lin), _ptr(s_swz),
                                                   _stream(a))

@@ -1,6 +1,6 @@
 """Build the HIP library quant_mxfp8_gemm_amd/libmxfp8_amd.so for gfx950 with hipcc.
 
-Every HIP source in csrc/ is compiled for gfx950 only, with packed-fp32 instruction
+Every HIP source in csrc/ (and the host-only checks.cpp) is compiled for gfx950 only, with packed-fp32 instruction
 selection turned off, then linked into one shared object exporting the C ABI of
 include/mxfp8.h. Objects go to _build/ (not part of the repository).
 """
@@ -26,11 +26,11 @@ CFLAGS = [
 
 
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
 def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+    obj = os.path.join(BUILD, os.path.splitext(os.path.basename(src))[0] + ".o")
     cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -46,7 +46,7 @@
 //  * Epilogue: the tile is converted to BF16 into LDS (over the stage buffers, rows padded by
 //    16 bytes) and written back with 16-byte streaming stores, every row a run of full lines.
 //  * A second epilogue serves the fused dense GEMM1 (gate_up projection, SiLU(gate) * up,
-//    MXFP8 quantisation; vLLM PR #65496 "Details", PR #64111 "Claims"): a tile's columns are
+//    MXFP8 quantisation; vLLM PR #64659 "Details", PR #64111 "Claims"): a tile's columns are
 //    half gate and half up for the same output columns, the fp32 accumulators meet in LDS and
 //    each thread turns one (row, 32-block) into E4M3 codes and a UE8M0 scale.
 #include <atomic>

@@ -188,3 +188,69 @@ def test_tiles_per_chunk(lib):
     assert mx.gemm_tiles_per_chunk(700, 6144, 4) == 2 * 32       # 96 x 192 for 175 rows (128 x 128 would give 2 x 48)
     assert mx.gemm_tiles_per_chunk(256, 6144, 1) == 4 * 48       # 64 x 128
     assert mx.gemm_tiles_per_chunk(128, 6144, 1) == 4 * 48       # 32 x 128
+
+
+# ---- the Python binding's own buffer checks (the C ABI cannot see buffer sizes)
+
+def _raises(fn, match):
+    with pytest.raises(ValueError, match=match):
+        fn()
+
+
+def test_binding_rejects_undersized_or_mislabelled_gemm_scales(lib):
+    import torch
+    m, n, k = 200, 64, 256
+    a = torch.zeros((m, k), dtype=torch.uint8)
+    b = torch.zeros((n, k), dtype=torch.uint8)
+    sa_lin = torch.zeros((m, k // 32), dtype=torch.uint8)
+    sb_swz = torch.zeros(mx.scale_bytes(n, k, mx.SWIZZLED), dtype=torch.uint8)
+    # linear [m, k/32] scales labelled swizzled: m % 128 != 0, so the buffer is too small
+    _raises(lambda: mx.gemm(a, sa_lin, mx.SWIZZLED, b, sb_swz, mx.SWIZZLED), "a_scales holds")
+    _raises(lambda: mx.gemm(a, sa_lin[:100], mx.LINEAR, b, sb_swz, mx.SWIZZLED), "a_scales holds")
+    _raises(lambda: mx.gemm(a, sa_lin, mx.LINEAR, b, sb_swz[:-1], mx.SWIZZLED), "b_scales holds")
+    _raises(lambda: mx.gemm(a, sa_lin, mx.LINEAR, b, sb_swz, 3), "scale layouts")
+    _raises(lambda: mx.gemm(a, sa_lin.float(), mx.LINEAR, b, sb_swz, mx.SWIZZLED), "contiguous uint8")
+    out = torch.zeros((m, n - 1), dtype=torch.bfloat16)
+    _raises(lambda: mx.gemm(a, sa_lin, mx.LINEAR, b, sb_swz, mx.SWIZZLED, out=out), r"out must be \[m, >=n\]")
+    bad_done = torch.zeros(2, dtype=torch.int32)
+    _raises(lambda: mx.gemm(a, sa_lin, mx.LINEAR, b, sb_swz, mx.SWIZZLED, num_chunks=4, chunk_done=bad_done),
+            "chunk_done")
+    # well-formed host tensors get as far as the placement check
+    _raises(lambda: mx.gemm(a, sa_lin, mx.LINEAR, b, sb_swz, mx.SWIZZLED), "GPU tensor")
+
+
+def test_binding_rejects_bad_quantiser_outputs(lib):
+    import torch
+    rows, k = 130, 256
+    x = torch.zeros((rows, k), dtype=torch.bfloat16)
+    w = torch.zeros(k, dtype=torch.bfloat16)
+    q = torch.zeros((rows, k), dtype=torch.uint8)
+    sl = torch.zeros((rows, k // 32), dtype=torch.uint8)
+    ss = torch.zeros(mx.scale_bytes(rows, k, mx.SWIZZLED), dtype=torch.uint8)
+    for call in (lambda out: mx.quantize(x, out=out), lambda out: mx.rmsnorm_quant(x, w, out=out),
+                 lambda out: mx.add_rmsnorm_quant(x, x.clone(), w, out=out)):
+        _raises(lambda: call((q[:-1], sl, ss)), "q must have shape")
+        _raises(lambda: call((q, sl[:-1], ss)), "scales_linear must have shape")
+        _raises(lambda: call((q, sl, ss[:-16])), "scales_swizzled holds")
+        _raises(lambda: call((q.t(), sl, ss)), "contiguous uint8")
+        _raises(lambda: call((q, None, None)), "at least one scale layout")
+        _raises(lambda: call((q, sl, ss)), "GPU tensor")
+    _raises(lambda: mx.quantize(torch.zeros((4, 48), dtype=torch.bfloat16)), "multiple of 32")
+
+
+def test_binding_rejects_bad_fused_gemm1_and_swizzle_buffers(lib):
+    import torch
+    m, inter, k = 64, 96, 256
+    a = torch.zeros((m, k), dtype=torch.uint8)
+    w = torch.zeros((2 * inter, k), dtype=torch.uint8)
+    sa = torch.zeros((m, k // 32), dtype=torch.uint8)
+    sw = torch.zeros(mx.scale_bytes(2 * inter, k, mx.SWIZZLED), dtype=torch.uint8)
+    _raises(lambda: mx.gemm_silu_mul_quant(a, sa, mx.SWIZZLED, w, sw, mx.SWIZZLED), "a_scales holds")
+    _raises(lambda: mx.gemm_silu_mul_quant(a, sa, mx.LINEAR, w, sw[:100], mx.SWIZZLED), "w_scales holds")
+    q = torch.zeros((m, inter), dtype=torch.uint8)
+    _raises(lambda: mx.gemm_silu_mul_quant(a, sa, mx.LINEAR, w, sw, mx.SWIZZLED,
+                                           out=(q, None, torch.zeros(10, dtype=torch.uint8))), "scales_swizzled holds")
+    _raises(lambda: mx.gemm_silu_mul_quant(a, sa, mx.LINEAR, w, sw, mx.SWIZZLED), "GPU tensor")
+    s_lin = torch.zeros((300, 6), dtype=torch.uint8)
+    _raises(lambda: mx.swizzle_scales(s_lin, out=torch.zeros(100, dtype=torch.uint8)), "out holds")
+    _raises(lambda: mx.swizzle_scales(s_lin), "GPU tensor")

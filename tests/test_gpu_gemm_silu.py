@@ -2,7 +2,8 @@
 * up, per-32 MXFP8 quantisation) against the oracle.
 
 Inputs are quantised by the oracle on the CPU. The kernel forms gate and up in the MFMA's fp32
-accumulators, whose error is bounded by MFMA_MASS_ERR times the dot product's absolute mass, so
+accumulators, whose error is bounded per element by the worst case of the MFMA's accumulation
+(parity_util.accum_error_bound: each group's truncation loss plus the fp32 summation bound), so
 its quantisation decisions may differ from the oracle's exact ones only within that bound: every
 scale must be reachable from an amax within the bound, every dequantised code must be a correct
 rounding of a value within the bound, and the share of decisions that differ must stay small.
@@ -16,7 +17,7 @@ import torch
 import oracle
 import quant_mxfp8_gemm_amd as mx
 import synth
-from parity_util import bits16, dev_u8, guard_intact, guarded_u8, silu_mul_quant_check
+from parity_util import accum_error_bound, bits16, dev_u8, guard_intact, guarded_u8, silu_mul_quant_check
 
 pytestmark = pytest.mark.gpu
 
@@ -43,12 +44,12 @@ def _run(qa, sa, la, qw, sw, lw):
 
 
 def _mass(qa, sa, la, qw, sw, lw, rows):
-    """sum_k |a_mk w_nk| for the listed rows and every column of the gate_up product."""
+    """The accumulation bound of every gate_up element of the listed rows (gate columns, then up)."""
     n = qw.shape[0]
     ri = np.repeat(np.asarray(rows, dtype=np.int64), n)
     ci = np.tile(np.arange(n, dtype=np.int64), len(rows))
-    _, f = oracle.gemm_sampled(qa & 0x7F, sa, la, qw & 0x7F, sw, lw, ri, ci)
-    return f.reshape(len(rows), n)
+    trunc, mass = oracle.gemm_accum_terms(qa, sa, la, qw, sw, lw, ri, ci)
+    return accum_error_bound(trunc, mass, qa.shape[1]).reshape(len(rows), n)
 
 
 # (m, inter, k, tile_m): one case per tile configuration (256 x 256, 256 x 192, 192 x 192,
