@@ -128,9 +128,17 @@ def cpu_baseline(target_s):
     rows = max(16, rows // 16 * 16)
     t = run(rows)
     flops = 2.0 * rows * N_MODEL * (K_DOWN + K_O)
-    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+    cores = oracle.num_threads()
+    # the same code on one thread, on a sample a sixteenth the size
+    prev = oracle.set_num_threads(1)
+    rows1 = max(16, rows // 16 // 16 * 16)
+    t1 = run(rows1)
+    oracle.set_num_threads(prev)
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"first {rows} of {M_CHAIN} rows of the step (norm rows scaled alike), fp64 oracle, "
-                      f"{t:.1f} s"}
+                      f"{t:.1f} s",
+            "one_thread": {"value": 2.0 * rows1 * N_MODEL * (K_DOWN + K_O) / t1 / 1e12, "unit": "TFLOP/s",
+                           "sample": f"first {rows1} rows, {t1:.1f} s"}}
 
 
 def main():
@@ -216,6 +224,11 @@ def main():
     def avg(a, b):
         return sum(events[i][a].elapsed_time(events[i][b]) for i in range(args.steps)) / args.steps / 1e3
 
+    def pct(a, b):
+        """Median, p10 and p90 of one kernel's event durations over the timed steps (seconds)."""
+        ts = sorted(events[i][a].elapsed_time(events[i][b]) / 1e3 for i in range(args.steps))
+        return ts[len(ts) // 2], ts[len(ts) // 10], ts[min(len(ts) - 1, (9 * len(ts)) // 10)]
+
     t_norm, t_qd, t_gd, t_qo, t_go = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4), avg(4, 5)
     ms_step = elapsed / args.steps * 1e3
     flops_d = 2.0 * M_CHAIN * N_MODEL * K_DOWN
@@ -223,7 +236,8 @@ def main():
     value = (flops_d + flops_o) / (elapsed / args.steps) / 1e12
     achieved = flops_d / t_gd / 1e12
     kernels = {
-        "rmsnorm_quant_1024x6144": {"us": t_norm * 1e6, "GB/s": norm_bytes(NORM_ROWS, N_MODEL) / t_norm / 1e9},
+        "rmsnorm_quant_1024x6144": {"us": t_norm * 1e6, "GB/s": norm_bytes(NORM_ROWS, N_MODEL) / t_norm / 1e9,
+                                    "frac_hbm": norm_bytes(NORM_ROWS, N_MODEL) / t_norm / 1e9 / PEAK_HBM_GBS},
         "quantize_32768x3072": {"us": t_qd * 1e6, "GB/s": quant_bytes(M_CHAIN, K_DOWN) / t_qd / 1e9,
                                 "frac_hbm": quant_bytes(M_CHAIN, K_DOWN) / t_qd / 1e9 / PEAK_HBM_GBS},
         "gemm_32768x6144x3072": {"us": t_gd * 1e6, "TFLOP/s": achieved, "frac_mfma": achieved / PEAK_MFMA_FP8_TFLOPS},
@@ -232,6 +246,12 @@ def main():
         "gemm_32768x6144x2048": {"us": t_go * 1e6, "TFLOP/s": flops_o / t_go / 1e12,
                                  "frac_mfma": flops_o / t_go / 1e12 / PEAK_MFMA_FP8_TFLOPS},
     }
+    # median / p10 / p90 of each kernel's event durations (microseconds) beside the means above
+    for name, (a, b) in (("rmsnorm_quant_1024x6144", (0, 1)), ("quantize_32768x3072", (1, 2)),
+                         ("gemm_32768x6144x3072", (2, 3)), ("quantize_32768x2048", (3, 4)),
+                         ("gemm_32768x6144x2048", (4, 5))):
+        med, p10, p90 = pct(a, b)
+        kernels[name].update({"us_median": med * 1e6, "us_p10": p10 * 1e6, "us_p90": p90 * 1e6})
     out = {
         "metric": METRIC,
         "value": round(value, 2),

@@ -77,6 +77,8 @@ def _load():
                                             c_i64p, c_i64p, i64, ctypes.c_int, c_dp, c_dp]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
+    lib.oracle_set_num_threads.restype = ctypes.c_int
+    lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
     _lib = lib
     return lib
 
@@ -95,6 +97,11 @@ def _check(rc, what):
 
 def num_threads() -> int:
     return _load().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> int:
+    """Threads for later oracle calls; returns the previous count."""
+    return _load().oracle_set_num_threads(int(n))
 
 
 def e4m3_value(code: int) -> float:

