@@ -45,6 +45,10 @@
 //    stage are one aligned dword in both scale layouts.
 //  * Epilogue: the tile is converted to BF16 into LDS (over the stage buffers, rows padded by
 //    16 bytes) and written back with 16-byte streaming stores, every row a run of full lines.
+//    The BF16 split-ring kernel instead issues the next tile's first loads before writing the
+//    tile out in four 32 KiB quarters through the two ring slots those loads leave free, and
+//    lets the stores drain under the next tile's first step: all 256 workgroups finish their
+//    tiles together, and their stores alone exceed what HBM takes in that time.
 //  * A second epilogue serves the fused dense GEMM1 (gate_up projection, SiLU(gate) * up,
 //    MXFP8 quantisation; vLLM PR #64659 "Details", PR #64111 "Claims"): a tile's columns are
 //    half gate and half up for the same output columns, the fp32 accumulators meet in LDS and
@@ -144,6 +148,61 @@ __device__ __forceinline__ uint32_t scale_base(uint32_t r, uint32_t nblk4) {
 // Distance between consecutive 128-K steps of one row's scale dwords.
 template <int LAYOUT>
 constexpr uint32_t scale_step() { return LAYOUT == 0 ? 4u : 512u; }
+
+// Fragment offsets inside a stage: the swizzle of row r + 32 t is that of row r with bit 2
+// flipped when t is odd (which swaps the two 64-K halves of the row), so four per-lane offsets
+// per operand, relative to the wave's first row, address every fragment read; the rest is a
+// constant (t * 32 rows).
+template <class T>
+__device__ __forceinline__ void frag_offsets(int wm, int wn, int l32, int g, int (&oa)[2][2], int (&ob)[2][2]) {
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      oa[kk][h] = lds_off(wm * T::WTM + l32, 4 * kk + 2 * h + g) - wm * T::WTM * 128;
+      ob[kk][h] = lds_off(wn * T::WTN + l32, 4 * kk + 2 * h + g) - wn * T::WTN * 128;
+    }
+}
+
+// One 128-K step of a wave's TM x TN blocks from LDS: two 64-K halves, each one scaled MFMA per
+// (B block, A block); between_halves runs after the first half's MFMAs are issued.
+template <class T, class F>
+__device__ __forceinline__ void lds_mma_step(v16f (&acc)[T::TN][T::TM], const uint8_t* a_lds, const uint8_t* b_lds,
+                                             int wm, int wn, const int (&oa)[2][2], const int (&ob)[2][2],
+                                             const uint32_t* as_sel, const uint32_t* bs_sel, F&& between_halves) {
+  const uint8_t* const a_w = a_lds + wm * T::WTM * 128;
+  const uint8_t* const b_w = b_lds + wn * T::WTN * 128;
+  // the compiler's predefined LDS-read / MFMA interleave (strategy 0) for this region
+  __builtin_amdgcn_iglp_opt(0);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    v8i af[T::TM], bf[T::TN];
+#pragma unroll
+    for (int t = 0; t < T::TM; ++t) {
+      const int kk = ks ^ (t & 1);
+      const v4i lo = *(const v4i*)(a_w + oa[kk][0] + t * 32 * 128);
+      const v4i hi = *(const v4i*)(a_w + oa[kk][1] + t * 32 * 128);
+      af[t] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int t = 0; t < T::TN; ++t) {
+      const int kk = ks ^ (t & 1);
+      const v4i lo = *(const v4i*)(b_w + ob[kk][0] + t * 32 * 128);
+      const v4i hi = *(const v4i*)(b_w + ob[kk][1] + t * 32 * 128);
+      bf[t] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int x = 0; x < T::TN; ++x)
+#pragma unroll
+      for (int y = 0; y < T::TM; ++y) {
+        if (ks == 0)
+          acc[x][y] = mfma<0>(bf[x], af[y], acc[x][y], (int)bs_sel[x], (int)as_sel[y]);
+        else
+          acc[x][y] = mfma<2>(bf[x], af[y], acc[x][y], (int)bs_sel[x], (int)as_sel[y]);
+      }
+    if (ks == 0) between_halves();
+  }
+}
 
 // Outputs of the fused dense GEMM1 epilogue (EPI_SWIGLU): B holds 2*inter rows, gate then up.
 struct SwiGluOut {
@@ -276,10 +335,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.f;
 
-    // Fragment offsets inside a stage: the swizzle of row r + 32 t is that of row r with bit 2
-    // flipped when t is odd (which swaps the two 64-K halves of the row), so four per-lane
-    // offsets per operand, relative to the wave's first row, address every fragment read; the
-    // rest is a constant (t * 32 rows).
+    // fragment offsets inside a stage (frag_offsets)
     int oa[2][2], ob[2][2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
@@ -288,42 +344,9 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
         oa[kk][h] = lds_off(wm * T::WTM + l32, 4 * kk + 2 * h + g) - wm * T::WTM * 128;
         ob[kk][h] = lds_off(wn * T::WTN + l32, 4 * kk + 2 * h + g) - wn * T::WTN * 128;
       }
-    // One 128-K step from LDS: two 64-K halves, each one scaled MFMA per (B block, A block);
-    // between_halves runs after the first half's MFMAs are issued
     auto mma_step = [&](const uint8_t* a_lds, const uint8_t* b_lds, const uint32_t* as_sel,
                         const uint32_t* bs_sel, auto&& between_halves) {
-      const uint8_t* const a_w = a_lds + wm * T::WTM * 128;
-      const uint8_t* const b_w = b_lds + wn * T::WTN * 128;
-      // the compiler's predefined LDS-read / MFMA interleave (strategy 0) for this region
-      __builtin_amdgcn_iglp_opt(0);
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        v8i af[T::TM], bf[T::TN];
-#pragma unroll
-        for (int t = 0; t < T::TM; ++t) {
-          const int kk = ks ^ (t & 1);
-          const v4i lo = *(const v4i*)(a_w + oa[kk][0] + t * 32 * 128);
-          const v4i hi = *(const v4i*)(a_w + oa[kk][1] + t * 32 * 128);
-          af[t] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-#pragma unroll
-        for (int t = 0; t < T::TN; ++t) {
-          const int kk = ks ^ (t & 1);
-          const v4i lo = *(const v4i*)(b_w + ob[kk][0] + t * 32 * 128);
-          const v4i hi = *(const v4i*)(b_w + ob[kk][1] + t * 32 * 128);
-          bf[t] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-#pragma unroll
-        for (int x = 0; x < T::TN; ++x)
-#pragma unroll
-          for (int y = 0; y < T::TM; ++y) {
-            if (ks == 0)
-              acc[x][y] = mfma<0>(bf[x], af[y], acc[x][y], (int)bs_sel[x], (int)as_sel[y]);
-            else
-              acc[x][y] = mfma<2>(bf[x], af[y], acc[x][y], (int)bs_sel[x], (int)as_sel[y]);
-          }
-        if (ks == 0) between_halves();
-      }
+      lds_mma_step<T>(acc, a_lds, b_lds, wm, wn, oa, ob, as_sel, bs_sel, between_halves);
     };
 
     if constexpr (T::SPLIT) {
@@ -636,6 +659,263 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
 }
 
 // Tile configurations: output tile, wave grid, LDS stages.
+// BF16-output GEMM on the split ring (256 x 256 tiles, swizzled scales), with the next tile's
+// first loads overlapping this tile's epilogue. After the last K step of a tile the workgroup
+// issues the next tile's A(0), B(0) and B(1) into A slot 0 and B slots 0 and 1, then writes the
+// BF16 tile out in four quarters of 128 rows x 128 columns (32 KiB each), staged alternately
+// in the two slots the next tile does not fill before its first step (A slot 1, B slot 2).
+// The C stores are buffer stores over the tile's own rows: an element past the last row or
+// column gets an offset past the resource and is dropped, so every wave issues the same 16
+// stores and the first step of the next tile can let exactly those stay in flight.
+template <class T>
+__global__ __launch_bounds__(T::NT, 1) void gemm_split_bf16_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, uint16_t* __restrict__ C, int M, int N, int K, int ldc, int num_chunks,
+    int first_chunk, int* __restrict__ chunk_done) {
+  static_assert(T::SPLIT && T::BM == 256 && T::BN == 256 && T::TM == 2 && T::TN == 4 && T::NT == 512 &&
+                    T::DA == 4 && T::DB == 4,
+                "split ring: 256 x 256 tiles of 8 waves of 64 x 128");
+  constexpr int BM = T::BM, BN = T::BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
+#if defined(__HIP_DEVICE_COMPILE__)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / (BN / T::WTN), wn = wave % (BN / T::WTN);
+  const int l32 = lane & 31, g = lane >> 5;
+
+  const int chunk_rows = M / num_chunks;
+  const int tiles_n = (N + BN - 1) / BN;
+  const int tiles_mc = (chunk_rows + BM - 1) / BM;
+  const int tpc = tiles_mc * tiles_n;
+  const int total = tpc * num_chunks;
+  const int KT = K / BK;
+  const uint32_t nblk4 = (uint32_t)K / 128;
+
+  uint8_t* const a_ring = smem;
+  uint8_t* const b_ring = smem + 2 * T::A_BYTES;
+  // epilogue staging: A slot 1 and B slot 2
+  uint8_t* const stage0 = a_ring + T::A_BYTES;
+  uint8_t* const stage1 = b_ring + 2 * T::B_BYTES;
+  const uint32_t sa_bytes = (uint32_t)((M + 127) / 128 * 128) * nblk4 * 4;
+  const uint32_t sb_bytes = (uint32_t)((N + 127) / 128 * 128) * nblk4 * 4;
+  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(As, sa_bytes), rsb = make_rsrc(Bs, sb_bytes);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(B, (uint32_t)N * (uint32_t)K);
+
+  // ---- per-tile state: output origin and the LDS-DMA / scale offsets of its loads
+  struct TileState {
+    int m0, m_end, n0, chunk;
+    uint32_t a_off[T::DA], b_off[T::DB], sa_off, sb_off;
+  };
+  auto setup = [&](int bid, TileState& ts) {
+    const int ci = bid / tpc;
+    const int j = bid - ci * tpc;
+    ts.chunk = (first_chunk + ci) % num_chunks;
+    const int lj = (tpc % 8 == 0) ? (j % 8) * (tpc / 8) + j / 8 : j;
+    const int group = lj / (GM * tiles_n);
+    const int first_tm = group * GM;
+    const int gsz = min(tiles_mc - first_tm, GM);
+    const int tm_idx = first_tm + (lj % (GM * tiles_n)) % gsz;
+    const int tn_idx = (lj % (GM * tiles_n)) / gsz;
+    const int chunk_m0 = ts.chunk * chunk_rows;
+    ts.m0 = chunk_m0 + tm_idx * BM;
+    ts.m_end = min(ts.m0 + BM, chunk_m0 + chunk_rows);
+    ts.n0 = tn_idx * BN;
+    // lane terms from an opaque copy of the lane index: recomputed per tile rather than kept
+    // live through the main loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int i = 0; i < T::DA; ++i) {
+      const int s = (wave * T::DA + i) * 64 + ln;
+      const int r = s >> 3;
+      ts.a_off[i] = (uint32_t)min(ts.m0 + r, M - 1) * (uint32_t)K + (((s & 7) ^ swz(r)) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < T::DB; ++i) {
+      const int s = (wave * T::DB + i) * 64 + ln;
+      const int r = s >> 3;
+      ts.b_off[i] = (uint32_t)min(ts.n0 + r, N - 1) * (uint32_t)K + (((s & 7) ^ swz(r)) * 16);
+    }
+    // rows r, r + 32, r + 64, r + 96 of a swizzled 128-row group keep their 4-byte scale groups
+    // side by side: one 8-byte load for the wave's two A row blocks, one 16-byte load for its
+    // four B row blocks (rows past the operand read zero padding or 0; not stored)
+    ts.sa_off = scale_base<1>((uint32_t)(ts.m0 + wm * T::WTM + (ln & 31)), nblk4);
+    ts.sb_off = scale_base<1>((uint32_t)(ts.n0 + wn * T::WTN + (ln & 31)), nblk4);
+  };
+  auto issue_a = [&](const TileState& ts, int kt) {
+    uint8_t* st = a_ring + (kt & 1) * T::A_BYTES;
+#pragma unroll
+    for (int i = 0; i < T::DA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + (wave * T::DA + i) * 1024), 16, ts.a_off[i],
+                                               (uint32_t)kt * BK, 0, 0);
+  };
+  auto issue_b = [&](const TileState& ts, int kt, int slot) {
+    uint8_t* st = b_ring + slot * T::B_BYTES;
+#pragma unroll
+    for (int i = 0; i < T::DB; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + (wave * T::DB + i) * 1024), 16, ts.b_off[i],
+                                               (uint32_t)kt * BK, 0, 0);
+  };
+  auto load_scales = [&](const TileState& ts, int kt, u32x2& sa, u32x4& sb) {
+    const int so = kt * (int)scale_step<1>();
+    sa = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsa, ts.sa_off, so, 0));
+    sb = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsb, ts.sb_off, so, 0));
+  };
+
+  int bid = blockIdx.x;
+  if (bid >= total) return;
+  TileState cur;
+  setup(bid, cur);
+  u32x2 sa;  // scales of the step about to run (loaded one step ahead)
+  u32x4 sb;
+  issue_b(cur, 0, 0);
+  issue_a(cur, 0);
+  load_scales(cur, 0, sa, sb);
+  issue_b(cur, 1, 1);
+  {
+    // 16 stores past the end of an empty resource (dropped): every tile's first step then
+    // finds the same 16 stores behind B(1)
+    const __amdgpu_buffer_rsrc_t none = make_rsrc(C, 0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0x80000000u + 16u * i, 0, 0);
+  }
+
+  while (true) {
+    // Per-tile lane constants, recomputed from an opaque copy of the lane index so that they
+    // are not kept live (in registers the epilogue needs) from one tile to the next.
+    int lane_t = lane;
+    asm volatile("" : "+v"(lane_t));
+    const int t32 = lane_t & 31, tg = lane_t >> 5;
+    int oa[2][2], ob[2][2];
+    frag_offsets<T>(wm, wn, t32, tg, oa, ob);
+    v16f acc[T::TN][T::TM];
+#pragma unroll
+    for (int x = 0; x < T::TN; ++x)
+#pragma unroll
+      for (int y = 0; y < T::TM; ++y)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.f;
+
+    int bslot = 0;  // B buffer of step kt
+    auto step = [&](int kt, bool next_a, bool next_b) {
+      block_barrier();
+      uint32_t as_sel[2], bs_sel[4];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) as_sel[t] = (sa[t] >> (8 * g)) & 0x00FF00FFu;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bs_sel[t] = (sb[t] >> (8 * g)) & 0x00FF00FFu;
+      const int refill = bslot == 0 ? 2 : bslot - 1;
+      const uint8_t* a_lds = a_ring + (kt & 1) * T::A_BYTES;
+      const uint8_t* b_lds = b_ring + bslot * T::B_BYTES;
+      bslot = bslot == 2 ? 0 : bslot + 1;
+      lds_mma_step<T>(acc, a_lds, b_lds, wm, wn, oa, ob, as_sel, bs_sel, [&] {
+        if (next_a) {
+          issue_a(cur, kt + 1);
+          load_scales(cur, kt + 1, sa, sb);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      });
+      if (next_b) issue_b(cur, kt + 2, refill);
+    };
+    // Step 0: A(0), B(0) and the scales have landed; B(1) and the 16 stores issued after it
+    // (the previous tile's C, or before the first tile 16 dropped ones) may still be in flight.
+    // With two K steps its B load for step 2 reads past K (inside B's resource, or 0) into
+    // B slot 2, which that tile never reads; the last step waits for it.
+    wait_vm<T::DB + 16>();
+    step(0, true, true);
+    for (int kt = 1; kt < KT - 2; ++kt) {
+      wait_vm<T::DB>();
+      step(kt, true, true);
+    }
+    if (KT > 2) {
+      wait_vm<T::DB>();
+      step(KT - 2, true, false);
+    }
+    wait_vm<0>();
+    step(KT - 1, false, false);
+
+    // ---- epilogue, with the next tile's first loads issued half-way
+    block_barrier();  // every wave is done reading the last stage
+    // lane terms of the epilogue from an opaque copy of the thread index (recomputed per tile
+    // rather than kept live, or spilled, through the main loop)
+    int tid_e = tid;
+    asm volatile("" : "+v"(tid_e));
+    const int e32 = tid_e & 31, eg = (tid_e >> 5) & 1;
+    // Quarter qd = (y, h): tile rows 64 wm + 32 y + [0, 32) of every wm and tile columns
+    // 128 wn + 64 h + [0, 64) of both wn, staged as 128 rows of 256 bytes (row 32 wm + l32,
+    // 16-byte chunk 8 wn + column / 8 within the half) with the chunk index xor-ed with row & 7,
+    // so that the 8-byte writes (32 rows) and the 16-byte reads (4 whole rows) of one
+    // instruction both spread evenly over the banks.
+    auto stage_quarter = [&](int qd, uint8_t* st) {
+      const int y = qd >> 1, h = qd & 1;
+      const int rq = wm * 32 + e32;
+#pragma unroll
+      for (int xx = 0; xx < 2; ++xx) {
+        const int x = 2 * h + xx;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int chunk = wn * 8 + xx * 4 + q;
+          const uint32_t lo = pack_bf16x2(acc[x][y][4 * q + 0], acc[x][y][4 * q + 1]);
+          const uint32_t hi = pack_bf16x2(acc[x][y][4 * q + 2], acc[x][y][4 * q + 3]);
+          *(uint2*)(st + rq * 256 + ((chunk ^ (rq & 7)) * 16) + eg * 8) = make_uint2(lo, hi);
+        }
+      }
+    };
+    // the first two quarters (half of the accumulators) go to LDS before the next tile's
+    // loads are issued, so that its offsets and this tile's remaining accumulators fit
+    stage_quarter(0, stage0);
+    stage_quarter(1, stage1);
+    const TileState done = cur;
+    const int nbid = bid + (int)gridDim.x;
+    const bool has_next = nbid < total;
+    if (has_next) {
+      setup(nbid, cur);
+      issue_b(cur, 0, 0);
+      issue_a(cur, 0);
+      load_scales(cur, 0, sa, sb);
+      issue_b(cur, 1, 1);
+    }
+    // C through a resource over this tile's rows: elements past the last row or column get an
+    // offset past its end and are dropped, so every wave issues the same 16 stores
+    const uint32_t c_bytes = (uint32_t)(done.m_end - done.m0) * (uint32_t)ldc * 2u;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(C + (int64_t)done.m0 * ldc, c_bytes);
+    auto store_quarter = [&](int qd, const uint8_t* st) {
+      const int y = qd >> 1, h = qd & 1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = tid_e + i * T::NT;
+        const int rq = p >> 4, chunk = p & 15;
+        const u32x4 v = *(const u32x4*)(st + rq * 256 + ((chunk ^ (rq & 7)) * 16));
+        const int r = (rq >> 5) * 64 + y * 32 + (rq & 31);  // tile row
+        const int n = done.n0 + (chunk >> 3) * 128 + h * 64 + (chunk & 7) * 8;
+        const bool ok = done.m0 + r < done.m_end && n < N;
+        const uint32_t off = ok ? ((uint32_t)r * (uint32_t)ldc + (uint32_t)n) * 2u : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 2);
+      }
+    };
+    block_barrier();
+    store_quarter(0, stage0);
+    store_quarter(1, stage1);
+    block_barrier();
+    stage_quarter(2, stage0);
+    stage_quarter(3, stage1);
+    block_barrier();
+    store_quarter(2, stage0);
+    store_quarter(3, stage1);
+
+    if (chunk_done != nullptr) {
+      __threadfence();  // this thread's C stores are visible device-wide
+      __syncthreads();
+      if (tid == 0) atomicAdd(chunk_done + done.chunk, 1);
+    }
+    if (!has_next) break;
+    bid = nbid;
+  }
+#endif
+}
+
 using TileL = Tile<256, 256, 4, 2, 2>;  // 8 waves of 64 x 128; large problems
 using TileLR = Tile<256, 256, 4, 2, 2, true>;  // the same with the split ring (swizzled scales)
 using TileN = Tile<256, 192, 4, 2, 2>;  // 8 waves of 64 x 96; when 256 x 256 leaves a round part-empty
@@ -748,6 +1028,13 @@ hipError_t launch_split(const uint8_t* a, const uint8_t* as, const uint8_t* b, c
   const int64_t tiles = tile_count(m, n, num_chunks, T::BM, T::BN);
   const int64_t grid = tiles < device_cu_count() ? tiles : device_cu_count();
   const int wide = ((uintptr_t)c % 16 == 0 && ldc % 8 == 0) ? 1 : 0;
+  // BF16 output in whole 16-byte segments, at least two K steps, tile offsets in 32 bits:
+  // the kernel that overlaps each epilogue with the next tile's first loads
+  if (EPI == EPI_BF16 && k >= 2 * BK && n % 8 == 0 && wide && (int64_t)ldc * 2 * T::BM < (1ll << 31)) {
+    gemm_split_bf16_kernel<T><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
+        a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
+    return hipGetLastError();
+  }
   gemm_kernel<T, 1, 1, EPI><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
       a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done, wide, sg);
   return hipGetLastError();

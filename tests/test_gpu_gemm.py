@@ -269,6 +269,24 @@ def test_gemm_o_proj_m32768():
     _workload_full(32768, 2048, mx.SWIZZLED, "act")
 
 
+@pytest.mark.parametrize("k", [256, 384])
+def test_gemm_split_ring_overlapped_epilogue(k):
+    """With 16-byte aligned output rows the BF16 split ring issues the next tile's first loads
+    before writing a tile out in quarters; with rows 8 bytes off that alignment it keeps the
+    plain epilogue. Two tiles per workgroup (512 tiles), two and three K steps, the last tile
+    row of each chunk a quarter tile short: both give the same bits, every chunk counts all its
+    tiles, and nothing lands outside C."""
+    m, n, chunks = 3968, 8000, 2
+    qa, sa, qb, sb = _operands(m, n, k, seed_a=k + 3, seed_b=k + 4)
+    done = torch.zeros(chunks, dtype=torch.int32, device="cuda")
+    c_ovl = _gpu_gemm(qa, sa[1], 1, qb, sb[1], 1, num_chunks=chunks, first_chunk=1, chunk_done=done, pad_cols=8)
+    c_plain = _gpu_gemm(qa, sa[1], 1, qb, sb[1], 1, num_chunks=chunks, first_chunk=1, pad_cols=4)
+    assert np.array_equal(c_ovl, c_plain)
+    assert done.cpu().tolist() == [mx.gemm_tiles_per_chunk(m, n, chunks)] * chunks == [256] * chunks
+    ref = oracle.gemm(qa, sa[1], 1, qb, sb[1], 1)
+    _assert_close(c_ovl, ref, _abs_sum_full(qa, sa[1], 1, qb, sb[1], 1), f"split ring overlapped k={k}")
+
+
 @pytest.mark.parametrize("m,n,k,chunks", [(64, 1, 128, 1), (33, 17, 256, 1), (200, 40, 16384, 2),
                                           (4, 300, 640, 4), (130, 3, 1152, 2)])
 def test_gemm_edge_shapes_full(m, n, k, chunks):
