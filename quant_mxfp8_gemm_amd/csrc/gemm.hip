@@ -776,7 +776,11 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_split_bf16_kernel(
   issue_b(cur, 1, 1);
   {
     // 16 stores past the end of an empty resource (dropped): every tile's first step then
-    // finds the same 16 stores behind B(1)
+    // finds the same 16 stores behind B(1). They must stay behind the loads above: the
+    // compiler may otherwise interleave them with those loads, and the first step's count
+    // would no longer cover B(0) and A(0).
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
     const __amdgpu_buffer_rsrc_t none = make_rsrc(C, 0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0x80000000u + 16u * i, 0, 0);
@@ -817,12 +821,12 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_split_bf16_kernel(
           __builtin_amdgcn_sched_barrier(0);
         }
       });
-      if (next_b) issue_b(cur, kt + 2, refill);
+      // (step 0 always refills, so that the compiler counts the same loads behind the scales on
+      // every path; with two K steps it reloads B(1) into slot 2, which that tile never reads)
+      if (next_b) issue_b(cur, min(kt + 2, KT - 1), refill);
     };
     // Step 0: A(0), B(0) and the scales have landed; B(1) and the 16 stores issued after it
     // (the previous tile's C, or before the first tile 16 dropped ones) may still be in flight.
-    // With two K steps its B load for step 2 reads past K (inside B's resource, or 0) into
-    // B slot 2, which that tile never reads; the last step waits for it.
     wait_vm<T::DB + 16>();
     step(0, true, true);
     for (int kt = 1; kt < KT - 2; ++kt) {

@@ -150,6 +150,26 @@ def test_gemm_split_ring_full(m, n, k, chunks):
     _assert_close(c, ref, _abs_sum_full(qa, sa[1], 1, qb, sb[1], 1), f"split ring m={m} k={k}")
 
 
+@pytest.mark.parametrize("k", [256, 1152])
+def test_gemm_split_ring_scale_layouts_agree(k):
+    """Both operands' scales swizzled take the split ring; any linear one the staged 256 x 256
+    kernel. With the same bytes behind them all four layout pairs give the same bits (two tiles
+    per workgroup, chunks ending a quarter tile short), and they match the oracle. Before each
+    product the same kernel runs on other operands, so that data read from LDS before its load
+    has landed would be that product's and show up here."""
+    m, n, chunks = 3968, 8000, 2
+    qa, sa, qb, sb = _operands(m, n, k, seed_a=k + 11, seed_b=k + 12)
+    xa, xsa, xb, xsb = _operands(m, n, k, seed_a=k + 21, seed_b=k + 22)
+    outs = {}
+    for la, lb in [(0, 0), (0, 1), (1, 0), (1, 1)]:
+        _gpu_gemm(xa, xsa[la], la, xb, xsb[lb], lb, num_chunks=chunks, first_chunk=1)
+        outs[(la, lb)] = _gpu_gemm(qa, sa[la], la, qb, sb[lb], lb, num_chunks=chunks, first_chunk=1)
+    for key, c in outs.items():
+        assert np.array_equal(c, outs[(1, 1)]), key
+    ref = oracle.gemm(qa, sa[0], 0, qb, sb[0], 0)
+    _assert_close(outs[(0, 0)], ref, _abs_sum_full(qa, sa[0], 0, qb, sb[0], 0), f"split ring linear k={k}")
+
+
 @pytest.mark.parametrize("k", [128, 640])
 def test_gemm_split_ring_matches_staged_path(k):
     """Scale buffers at an address that is 4 but not 16 bytes aligned send the same product
