@@ -53,8 +53,8 @@ def _parse():
 # counter of a 1 GiB copy onto 1 GiB. Valid only for the kernel code it was taken on
 # (gemm_code_sha256).
 GEMM_TRAFFIC = {
-    "source_sha256": "5f8c7f1e095d0d1c66ad08900020b3929041501a6ea1efa762e77f777ee75e21",
-    "fetch_kib": 456273.9, "write_kib": 393507.5,
+    "source_sha256": "cdc15f473c986d6f27b65257a320a60d078080ff3d0765ce6d6160283688e51f",
+    "fetch_kib": 456275.5, "write_kib": 393452.2,
     "fetch_factor": 2.0, "write_factor": 1.0,
 }
 
