@@ -298,7 +298,10 @@ def test_gemm_split_ring_overlapped_epilogue(k):
     tiles, and nothing lands outside C."""
     m, n, chunks = 3968, 8000, 2
     qa, sa, qb, sb = _operands(m, n, k, seed_a=k + 3, seed_b=k + 4)
+    xa, xsa, xb, xsb = _operands(m, n, k, seed_a=k + 5, seed_b=k + 6)
     done = torch.zeros(chunks, dtype=torch.int32, device="cuda")
+    # a decoy product first: data read from LDS before its load has landed would be its data
+    _gpu_gemm(xa, xsa[1], 1, xb, xsb[1], 1, num_chunks=chunks, first_chunk=1, pad_cols=8)
     c_ovl = _gpu_gemm(qa, sa[1], 1, qb, sb[1], 1, num_chunks=chunks, first_chunk=1, chunk_done=done, pad_cols=8)
     c_plain = _gpu_gemm(qa, sa[1], 1, qb, sb[1], 1, num_chunks=chunks, first_chunk=1, pad_cols=4)
     assert np.array_equal(c_ovl, c_plain)
