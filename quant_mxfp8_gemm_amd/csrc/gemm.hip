@@ -21,10 +21,14 @@
 //  * With swizzled, 16-byte aligned scales the 256 x 256 tile runs a split ring: A in two
 //    stage buffers and B in three (B fetched two steps ahead, all 160 KiB of LDS), the scales
 //    of a wave's rows loaded one step ahead into registers with one 8-byte and one 16-byte
-//    load (rows r, r+32, r+64, r+96 of a swizzled 128-row group are adjacent). Its A refill
-//    (and the refills of the staged tiles of up to 128 rows) is issued between the two 64-K
-//    halves of a step and its B refill after the step's MFMAs, so the step's first fragment
-//    reads and MFMAs follow the barrier at once. With at most 32 rows in one chunk (decode)
+//    load (rows r, r+32, r+64, r+96 of a swizzled 128-row group are adjacent). With BF16
+//    output in whole 16-byte segments it runs as two wave groups that take turns on each
+//    SIMD's matrix pipe (one issues a half step's MFMAs from registers while the other reads
+//    its next fragments from LDS and issues the loads), with a barrier between turns
+//    (gemm_pingpong_bf16_kernel). Otherwise (the fused gate_up epilogue, unaligned output)
+//    its A refill (and the refills of the staged tiles of up to 128 rows) is issued between
+//    the two 64-K halves of a step and its B refill after the step's MFMAs, so the step's
+//    first fragment reads and MFMAs follow the barrier at once. With at most 32 rows in one chunk (decode)
 //    the BF16 GEMM uses one-wave 32 x 32 tiles whose fragments and scales go straight from memory
 //    into registers, eight K steps ahead, with no LDS stages or barriers. Every other case uses
 //    NS-stage buffers holding A, B and the scale dwords together. All give the same bits:
@@ -45,7 +49,7 @@
 //    stage are one aligned dword in both scale layouts.
 //  * Epilogue: the tile is converted to BF16 into LDS (over the stage buffers, rows padded by
 //    16 bytes) and written back with 16-byte streaming stores, every row a run of full lines.
-//    The BF16 split-ring kernel instead issues the next tile's first loads before writing the
+//    The two-group BF16 kernel instead issues the next tile's first loads before writing the
 //    tile out in four 32 KiB quarters through the two ring slots those loads leave free, and
 //    lets the stores drain under the next tile's first step: all 256 workgroups finish their
 //    tiles together, and their stores alone exceed what HBM takes in that time.
@@ -54,6 +58,7 @@
 //    half gate and half up for the same output columns, the fp32 accumulators meet in LDS and
 //    each thread turns one (row, 32-block) into E4M3 codes and a UE8M0 scale.
 #include <atomic>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -659,30 +664,53 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
 }
 
 // Tile configurations: output tile, wave grid, LDS stages.
-// BF16-output GEMM on the split ring (256 x 256 tiles, swizzled scales), with the next tile's
-// first loads overlapping this tile's epilogue. After the last K step of a tile the workgroup
-// issues the next tile's A(0), B(0) and B(1) into A slot 0 and B slots 0 and 1, then writes the
-// BF16 tile out in four quarters of 128 rows x 128 columns (32 KiB each), staged alternately
-// in the two slots the next tile does not fill before its first step (A slot 1, B slot 2).
-// The C stores are buffer stores over the tile's own rows: an element past the last row or
-// column gets an offset past the resource and is dropped, so every wave issues the same 16
-// stores and the first step of the next tile can let exactly those stay in flight.
+// BF16-output GEMM on 256 x 256 tiles whose eight waves take turns on the matrix pipes. Waves
+// 0-3 (tile rows 0-127) and waves 4-7 (rows 128-255) put one wave of each group on every SIMD.
+// Each wave alternates a memory phase (the LDS fragment reads of one 64-K half step into
+// registers, then its share of the loads) and a compute phase (the half step's eight scaled
+// MFMAs from those registers), with a workgroup barrier after every phase; the second group
+// starts one phase late, so that on each SIMD one wave issues MFMAs while the other reads its
+// next fragments. B is in a ring of three LDS slots (fetched two steps ahead) and A in two (one
+// step ahead), the scales in registers one step ahead. Each group loads the A rows that only it
+// reads, so the refill of an A slot waits only for that group's last reads of it.
+//  * A memory phase issues no vector ALU work: an MFMA waiting for the matrix pipe holds the
+//    SIMD's vector issue, so ALU work in one wave's memory phase would wait on the other wave's
+//    MFMAs. The LDS addresses are per-lane bases fixed for the tile plus instruction offsets;
+//    the loop is unrolled over six steps (two A slots, three B slots, two scale register sets)
+//    so that every slot offset is a constant.
+//  * A load instruction can take hundreds of cycles to issue when the memory pipeline is busy,
+//    so the loads are issued in the memory phases, after the fragment reads.
+//  * Per step and wave the loads leave in one order (scales of step s + 1, A(s + 1), B(s + 2)),
+//    so that two fixed counts wait for B(s + 1) before the last barrier that precedes its first
+//    read and for A(s + 1) before the group's own first read. Loads past the last step go
+//    through empty resources (dropped) so that the counts hold on every path.
+//  * After the last step of a tile the workgroup issues the next tile's B(0), scales, A(0) and
+//    B(1) (A slot 0, B slots 0 and 1), then writes the BF16 tile out in four quarters of
+//    128 rows x 128 columns staged alternately in A slot 1 and B slot 2. The C stores are
+//    buffer stores over the tile's own rows (elements past the last row or column are dropped),
+//    so every wave issues the same 16 stores, and the next tile's first waits let exactly those
+//    stay in flight.
 template <class T>
-__global__ __launch_bounds__(T::NT, 1) void gemm_split_bf16_kernel(
+__global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, uint16_t* __restrict__ C, int M, int N, int K, int ldc, int num_chunks,
     int first_chunk, int* __restrict__ chunk_done) {
   static_assert(T::SPLIT && T::BM == 256 && T::BN == 256 && T::TM == 2 && T::TN == 4 && T::NT == 512 &&
-                    T::DA == 4 && T::DB == 4,
-                "split ring: 256 x 256 tiles of 8 waves of 64 x 128");
+                    T::DA == 4 && T::DB == 4 && T::WTM == 64 && T::WTN == 128 && T::B_BYTES == 32768 &&
+                    T::A_BYTES == 32768,
+                "256 x 256 tiles of 8 waves of 64 x 128");
   constexpr int BM = T::BM, BN = T::BN;
+  // B slots at 0, 32 and 64 KiB, A slots at 96 and 128 KiB
+  constexpr int B_RING = 0, A_RING = 3 * T::B_BYTES;
+  constexpr int C_STORES = 16;  // C stores per thread and tile
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
 #if defined(__HIP_DEVICE_COMPILE__)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;  // 0: tile rows 0-127, 1: rows 128-255
   const int wm = wave / (BN / T::WTN), wn = wave % (BN / T::WTN);
-  const int l32 = lane & 31, g = lane >> 5;
+  const int g = lane >> 5;
 
   const int chunk_rows = M / num_chunks;
   const int tiles_n = (N + BN - 1) / BN;
@@ -692,18 +720,14 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_split_bf16_kernel(
   const int KT = K / BK;
   const uint32_t nblk4 = (uint32_t)K / 128;
 
-  uint8_t* const a_ring = smem;
-  uint8_t* const b_ring = smem + 2 * T::A_BYTES;
-  // epilogue staging: A slot 1 and B slot 2
-  uint8_t* const stage0 = a_ring + T::A_BYTES;
-  uint8_t* const stage1 = b_ring + 2 * T::B_BYTES;
   const uint32_t sa_bytes = (uint32_t)((M + 127) / 128 * 128) * nblk4 * 4;
   const uint32_t sb_bytes = (uint32_t)((N + 127) / 128 * 128) * nblk4 * 4;
-  const __amdgpu_buffer_rsrc_t rsa = make_rsrc(As, sa_bytes), rsb = make_rsrc(Bs, sb_bytes);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A, (uint32_t)M * (uint32_t)K);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(B, (uint32_t)N * (uint32_t)K);
+  const uint32_t a_bytes = (uint32_t)M * (uint32_t)K, b_bytes = (uint32_t)N * (uint32_t)K;
+  // epilogue staging: A slot 1 and B slot 2 (the next tile's first loads use the other slots)
+  uint8_t* const stage0 = smem + A_RING + T::A_BYTES;
+  uint8_t* const stage1 = smem + B_RING + 2 * T::B_BYTES;
 
-  // ---- per-tile state: output origin and the LDS-DMA / scale offsets of its loads
+  // ---- per-tile state: output origin and the offsets of its loads
   struct TileState {
     int m0, m_end, n0, chunk;
     uint32_t a_off[T::DA], b_off[T::DB], sa_off, sb_off;
@@ -728,15 +752,17 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_split_bf16_kernel(
     asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < T::DA; ++i) {
-      const int s = (wave * T::DA + i) * 64 + ln;
-      const int r = s >> 3;
-      ts.a_off[i] = (uint32_t)min(ts.m0 + r, M - 1) * (uint32_t)K + (((s & 7) ^ swz(r)) * 16);
+      // LDS kilobyte wave * DA + i of an A slot holds tile rows 32 wave + 8 i + [0, 8): waves
+      // 0-3 fill rows 0-127, waves 4-7 rows 128-255, the rows their own group reads
+      const int sidx = (wave * T::DA + i) * 64 + ln;
+      const int r = sidx >> 3;
+      ts.a_off[i] = (uint32_t)min(ts.m0 + r, M - 1) * (uint32_t)K + (((sidx & 7) ^ swz(r)) * 16);
     }
 #pragma unroll
     for (int i = 0; i < T::DB; ++i) {
-      const int s = (wave * T::DB + i) * 64 + ln;
-      const int r = s >> 3;
-      ts.b_off[i] = (uint32_t)min(ts.n0 + r, N - 1) * (uint32_t)K + (((s & 7) ^ swz(r)) * 16);
+      const int sidx = (wave * T::DB + i) * 64 + ln;
+      const int r = sidx >> 3;
+      ts.b_off[i] = (uint32_t)min(ts.n0 + r, N - 1) * (uint32_t)K + (((sidx & 7) ^ swz(r)) * 16);
     }
     // rows r, r + 32, r + 64, r + 96 of a swizzled 128-row group keep their 4-byte scale groups
     // side by side: one 8-byte load for the wave's two A row blocks, one 16-byte load for its
@@ -744,56 +770,86 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_split_bf16_kernel(
     ts.sa_off = scale_base<1>((uint32_t)(ts.m0 + wm * T::WTM + (ln & 31)), nblk4);
     ts.sb_off = scale_base<1>((uint32_t)(ts.n0 + wn * T::WTN + (ln & 31)), nblk4);
   };
-  auto issue_a = [&](const TileState& ts, int kt) {
-    uint8_t* st = a_ring + (kt & 1) * T::A_BYTES;
+  // loads past the last step go through empty resources: dropped, but counted like the others
+  auto issue_a = [&](const TileState& ts, int kt, int slot) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(A, kt < KT ? a_bytes : 0u);
+    uint8_t* st = smem + A_RING + slot * T::A_BYTES;
 #pragma unroll
     for (int i = 0; i < T::DA; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void*)(st + (wave * T::DA + i) * 1024), 16, ts.a_off[i],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(st + (wave * T::DA + i) * 1024), 16, ts.a_off[i],
                                                (uint32_t)kt * BK, 0, 0);
   };
   auto issue_b = [&](const TileState& ts, int kt, int slot) {
-    uint8_t* st = b_ring + slot * T::B_BYTES;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(B, kt < KT ? b_bytes : 0u);
+    uint8_t* st = smem + B_RING + slot * T::B_BYTES;
 #pragma unroll
     for (int i = 0; i < T::DB; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void*)(st + (wave * T::DB + i) * 1024), 16, ts.b_off[i],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(st + (wave * T::DB + i) * 1024), 16, ts.b_off[i],
                                                (uint32_t)kt * BK, 0, 0);
   };
   auto load_scales = [&](const TileState& ts, int kt, u32x2& sa, u32x4& sb) {
-    const int so = kt * (int)scale_step<1>();
-    sa = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsa, ts.sa_off, so, 0));
-    sb = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsb, ts.sb_off, so, 0));
+    const bool live = kt < KT;
+    const int so = live ? kt * (int)scale_step<1>() : 0;
+    sa = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(make_rsrc(As, live ? sa_bytes : 0u), ts.sa_off, so, 0));
+    sb = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(Bs, live ? sb_bytes : 0u), ts.sb_off, so, 0));
+  };
+  // a tile's first loads, in the loop's order (B(s + 1) issued last before step s), so that the
+  // counts and the compiler's own waits for the scales see the same loads in flight
+  auto first_loads = [&](const TileState& ts, u32x2& sa, u32x4& sb) {
+    issue_b(ts, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_scales(ts, 0, sa, sb);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_a(ts, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b(ts, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // end of a phase: nothing moves across it, and every wave's LDS reads have completed
+  auto phase_end = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    block_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   int bid = blockIdx.x;
   if (bid >= total) return;
   TileState cur;
   setup(bid, cur);
-  u32x2 sa;  // scales of the step about to run (loaded one step ahead)
-  u32x4 sb;
-  issue_b(cur, 0, 0);
-  issue_a(cur, 0);
-  load_scales(cur, 0, sa, sb);
-  issue_b(cur, 1, 1);
+  u32x2 sa2[2];
+  u32x4 sb2[2];
+  first_loads(cur, sa2[0], sb2[0]);
   {
-    // 16 stores past the end of an empty resource (dropped): every tile's first step then
-    // finds the same 16 stores behind B(1). They must stay behind the loads above: the
-    // compiler may otherwise interleave them with those loads, and the first step's count
-    // would no longer cover B(0) and A(0).
+    // 16 stores past the end of an empty resource (dropped): every tile then starts with the
+    // same 16 stores behind its first loads. They must stay behind those loads: the compiler
+    // may otherwise interleave them, and the first counts would no longer cover the loads.
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
     const __amdgpu_buffer_rsrc_t none = make_rsrc(C, 0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0x80000000u + 16u * i, 0, 0);
+    for (int i = 0; i < C_STORES; ++i) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0x80000000u + 16u * i, 0, 0);
   }
 
   while (true) {
-    // Per-tile lane constants, recomputed from an opaque copy of the lane index so that they
-    // are not kept live (in registers the epilogue needs) from one tile to the next.
-    int lane_t = lane;
-    asm volatile("" : "+v"(lane_t));
-    const int t32 = lane_t & 31, tg = lane_t >> 5;
-    int oa[2][2], ob[2][2];
-    frag_offsets<T>(wm, wn, t32, tg, oa, ob);
+    // per-lane LDS bases of the fragment reads: A slot 0 (slot 1 at +32 KiB), B slots 0 and 1
+    // (+32 KiB) and B slot 2; the block offsets t * 4 KiB and the slot offsets are instruction
+    // offsets (below 64 KiB). From an opaque copy of the lane index, per tile.
+    int va[2][2], vb[2][2], vb2[2][2];
+    {
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      int oa[2][2], ob[2][2];
+      frag_offsets<T>(wm, wn, ln & 31, ln >> 5, oa, ob);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          va[kk][h] = A_RING + wm * T::WTM * 128 + oa[kk][h];
+          vb[kk][h] = B_RING + wn * T::WTN * 128 + ob[kk][h];
+          vb2[kk][h] = vb[kk][h] + 2 * T::B_BYTES;
+          asm volatile("" : "+v"(va[kk][h]), "+v"(vb[kk][h]), "+v"(vb2[kk][h]));
+        }
+    }
     v16f acc[T::TN][T::TM];
 #pragma unroll
     for (int x = 0; x < T::TN; ++x)
@@ -802,48 +858,118 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_split_bf16_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.f;
 
-    int bslot = 0;  // B buffer of step kt
-    auto step = [&](int kt, bool next_a, bool next_b) {
-      block_barrier();
-      uint32_t as_sel[2], bs_sel[4];
+    // fragments of one 64-K half step (ks) from A slot sa_slot and B slot sb_slot
+    auto read_frags = [&](int sa_slot, int sb_slot, int ks, v8i (&af)[T::TM], v8i (&bf)[T::TN]) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) as_sel[t] = (sa[t] >> (8 * g)) & 0x00FF00FFu;
+      for (int t = 0; t < T::TM; ++t) {
+        const int kk = ks ^ (t & 1);
+        const uint8_t* p0 = smem + va[kk][0] + sa_slot * T::A_BYTES + t * 32 * 128;
+        const uint8_t* p1 = smem + va[kk][1] + sa_slot * T::A_BYTES + t * 32 * 128;
+        const v4i lo = *(const v4i*)p0, hi = *(const v4i*)p1;
+        af[t] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) bs_sel[t] = (sb[t] >> (8 * g)) & 0x00FF00FFu;
-      const int refill = bslot == 0 ? 2 : bslot - 1;
-      const uint8_t* a_lds = a_ring + (kt & 1) * T::A_BYTES;
-      const uint8_t* b_lds = b_ring + bslot * T::B_BYTES;
-      bslot = bslot == 2 ? 0 : bslot + 1;
-      lds_mma_step<T>(acc, a_lds, b_lds, wm, wn, oa, ob, as_sel, bs_sel, [&] {
-        if (next_a) {
-          issue_a(cur, kt + 1);
-          load_scales(cur, kt + 1, sa, sb);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      });
-      // (step 0 always refills, so that the compiler counts the same loads behind the scales on
-      // every path; with two K steps it reloads B(1) into slot 2, which that tile never reads)
-      if (next_b) issue_b(cur, min(kt + 2, KT - 1), refill);
+      for (int t = 0; t < T::TN; ++t) {
+        const int kk = ks ^ (t & 1);
+        const int b0 = sb_slot == 2 ? vb2[kk][0] : vb[kk][0] + sb_slot * T::B_BYTES;
+        const int b1 = sb_slot == 2 ? vb2[kk][1] : vb[kk][1] + sb_slot * T::B_BYTES;
+        const v4i lo = *(const v4i*)(smem + b0 + t * 32 * 128), hi = *(const v4i*)(smem + b1 + t * 32 * 128);
+        bf[t] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
     };
-    // Step 0: A(0), B(0) and the scales have landed; B(1) and the 16 stores issued after it
-    // (the previous tile's C, or before the first tile 16 dropped ones) may still be in flight.
-    wait_vm<T::DB + 16>();
-    step(0, true, true);
-    for (int kt = 1; kt < KT - 2; ++kt) {
+    // the half step's MFMAs; scale byte 0 (first 64 K) or 2 (second 64 K) of this lane's block g
+    auto mma_half = [&](int ks, const v8i (&af)[T::TM], const v8i (&bf)[T::TN], const u32x2& sa, const u32x4& sb) {
+      uint32_t as_sel[T::TM], bs_sel[T::TN];
+#pragma unroll
+      for (int t = 0; t < T::TM; ++t) as_sel[t] = (sa[t] >> (8 * g)) & 0x00FF00FFu;
+#pragma unroll
+      for (int t = 0; t < T::TN; ++t) bs_sel[t] = (sb[t] >> (8 * g)) & 0x00FF00FFu;
+#pragma unroll
+      for (int x = 0; x < T::TN; ++x)
+#pragma unroll
+        for (int y = 0; y < T::TM; ++y) {
+          if (ks == 0)
+            acc[x][y] = mfma<0>(bf[x], af[y], acc[x][y], (int)bs_sel[x], (int)as_sel[y]);
+          else
+            acc[x][y] = mfma<2>(bf[x], af[y], acc[x][y], (int)bs_sel[x], (int)as_sel[y]);
+        }
+    };
+    // One 128-K step s (J = s mod 6) as four phases. First memory phase: the fragments, then the
+    // scales of step s + 1 and A(s + 1) (into this group's rows of the slot of step s - 1, which
+    // the group has finished reading). Second memory phase: the fragments, then B(s + 2) (into
+    // the slot of step s - 1, which both groups have finished reading). In a tile's first step
+    // the previous tile's 16 C stores may still be in flight behind B(1).
+    auto stage = [&](auto Jc, int s, auto First) {
+      constexpr int J = decltype(Jc)::value;
+      constexpr bool FIRST = decltype(First)::value;
+      constexpr int AS = J & 1, BS = J % 3, CUR = J & 1, NXT = (J + 1) & 1;
+      v8i af[T::TM], bf[T::TN];
+      // memory, first half
+      read_frags(AS, BS, 0, af, bf);
+      __builtin_amdgcn_sched_barrier(0);
+      load_scales(cur, s + 1, sa2[NXT], sb2[NXT]);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_a(cur, s + 1, AS ^ 1);
+      phase_end();
+      // compute, first half
+      __builtin_amdgcn_s_setprio(1);
+      mma_half(0, af, bf, sa2[CUR], sb2[CUR]);
+      __builtin_amdgcn_s_setprio(0);
+      phase_end();
+      // memory, second half; then B(s + 1) has landed (behind it: the scales of s + 1, A(s + 1)
+      // and B(s + 2)), before the barrier after which the first group reads it
+      read_frags(AS, BS, 1, af, bf);
+      __builtin_amdgcn_sched_barrier(0);
+      issue_b(cur, s + 2, (J + 2) % 3);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (FIRST)
+        wait_vm<C_STORES + 2 + T::DA + T::DB>();
+      else
+        wait_vm<2 + T::DA + T::DB>();
+      phase_end();
+      // compute, second half; then A(s + 1) has landed (behind it: B(s + 2)), before the barrier
+      // after which this group reads it
+      __builtin_amdgcn_s_setprio(1);
+      mma_half(1, af, bf, sa2[CUR], sb2[CUR]);
+      __builtin_amdgcn_s_setprio(0);
+      __builtin_amdgcn_sched_barrier(0);
       wait_vm<T::DB>();
-      step(kt, true, true);
+      phase_end();
+    };
+    // B(0), the scales of step 0 and A(0) have landed; B(1) and the 16 C stores issued after it
+    // (the previous tile's, or before the first tile 16 dropped ones) may still be in flight
+    wait_vm<T::DB + C_STORES>();
+    phase_end();
+    if (grp) phase_end();  // the second group starts one phase late
+    // The first step on its own (its count lets the previous tile's C stores stay in flight),
+    // then six steps per iteration, left after the last step wherever it falls (a wait count
+    // chosen at run time inside a step would split it, and the compiler then spills)
+    using No = std::integral_constant<bool, false>;
+    stage(std::integral_constant<int, 0>{}, 0, std::integral_constant<bool, true>{});
+    if (KT > 1) {
+      for (int s = 1;; s += 6) {
+        stage(std::integral_constant<int, 1>{}, s, No{});
+        if (s + 1 >= KT) break;
+        stage(std::integral_constant<int, 2>{}, s + 1, No{});
+        if (s + 2 >= KT) break;
+        stage(std::integral_constant<int, 3>{}, s + 2, No{});
+        if (s + 3 >= KT) break;
+        stage(std::integral_constant<int, 4>{}, s + 3, No{});
+        if (s + 4 >= KT) break;
+        stage(std::integral_constant<int, 5>{}, s + 4, No{});
+        if (s + 5 >= KT) break;
+        stage(std::integral_constant<int, 0>{}, s + 5, No{});
+        if (s + 6 >= KT) break;
+      }
     }
-    if (KT > 2) {
-      wait_vm<T::DB>();
-      step(KT - 2, true, false);
-    }
-    wait_vm<0>();
-    step(KT - 1, false, false);
+    if (!grp) phase_end();  // the first group meets the second group's last barrier
+    wait_vm<0>();           // the dropped loads too: nothing writes LDS under the epilogue
+    // the scale registers stay live past the loop: otherwise the compiler sinks each step's scale
+    // loads into the next step (their only use, behind an early exit), right before the MFMAs
+    asm volatile("" ::"v"(sa2[0]), "v"(sa2[1]), "v"(sb2[0]), "v"(sb2[1]));
 
     // ---- epilogue, with the next tile's first loads issued half-way
-    block_barrier();  // every wave is done reading the last stage
-    // lane terms of the epilogue from an opaque copy of the thread index (recomputed per tile
-    // rather than kept live, or spilled, through the main loop)
+    block_barrier();  // every wave's loads have landed and its reads are done
     int tid_e = tid;
     asm volatile("" : "+v"(tid_e));
     const int e32 = tid_e & 31, eg = (tid_e >> 5) & 1;
@@ -867,8 +993,8 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_split_bf16_kernel(
         }
       }
     };
-    // the first two quarters (half of the accumulators) go to LDS before the next tile's
-    // loads are issued, so that its offsets and this tile's remaining accumulators fit
+    // the first two quarters (half of the accumulators) go to LDS before the next tile's loads
+    // are issued, so that its offsets and this tile's remaining accumulators fit
     stage_quarter(0, stage0);
     stage_quarter(1, stage1);
     const TileState done = cur;
@@ -876,10 +1002,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_split_bf16_kernel(
     const bool has_next = nbid < total;
     if (has_next) {
       setup(nbid, cur);
-      issue_b(cur, 0, 0);
-      issue_a(cur, 0);
-      load_scales(cur, 0, sa, sb);
-      issue_b(cur, 1, 1);
+      first_loads(cur, sa2[0], sb2[0]);
     }
     // C through a resource over this tile's rows: elements past the last row or column get an
     // offset past its end and are dropped, so every wave issues the same 16 stores
@@ -1032,10 +1155,10 @@ hipError_t launch_split(const uint8_t* a, const uint8_t* as, const uint8_t* b, c
   const int64_t tiles = tile_count(m, n, num_chunks, T::BM, T::BN);
   const int64_t grid = tiles < device_cu_count() ? tiles : device_cu_count();
   const int wide = ((uintptr_t)c % 16 == 0 && ldc % 8 == 0) ? 1 : 0;
-  // BF16 output in whole 16-byte segments, at least two K steps, tile offsets in 32 bits:
-  // the kernel that overlaps each epilogue with the next tile's first loads
+  // BF16 output in whole 16-byte segments, at least two K steps, tile offsets in 32 bits: the
+  // two-group kernel, which also overlaps each epilogue with the next tile's first loads
   if (EPI == EPI_BF16 && k >= 2 * BK && n % 8 == 0 && wide && (int64_t)ldc * 2 * T::BM < (1ll << 31)) {
-    gemm_split_bf16_kernel<T><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
+    gemm_pingpong_bf16_kernel<T><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
         a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
     return hipGetLastError();
   }

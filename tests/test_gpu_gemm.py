@@ -291,11 +291,12 @@ def test_gemm_o_proj_m32768():
 
 @pytest.mark.parametrize("k", [256, 384])
 def test_gemm_split_ring_overlapped_epilogue(k):
-    """With 16-byte aligned output rows the BF16 split ring issues the next tile's first loads
-    before writing a tile out in quarters; with rows 8 bytes off that alignment it keeps the
-    plain epilogue. Two tiles per workgroup (512 tiles), two and three K steps, the last tile
-    row of each chunk a quarter tile short: both give the same bits, every chunk counts all its
-    tiles, and nothing lands outside C."""
+    """With 16-byte aligned output rows the 256 x 256 BF16 GEMM runs the two-group kernel,
+    which issues the next tile's first loads before writing a tile out in quarters; with rows
+    8 bytes off that alignment it runs the split ring with the plain epilogue. Two tiles per
+    workgroup (512 tiles), two and three K steps, the last tile row of each chunk a quarter tile
+    short: both give the same bits, every chunk counts all its tiles, and nothing lands
+    outside C."""
     m, n, chunks = 3968, 8000, 2
     qa, sa, qb, sb = _operands(m, n, k, seed_a=k + 3, seed_b=k + 4)
     xa, xsa, xb, xsb = _operands(m, n, k, seed_a=k + 5, seed_b=k + 6)
@@ -308,6 +309,27 @@ def test_gemm_split_ring_overlapped_epilogue(k):
     assert done.cpu().tolist() == [mx.gemm_tiles_per_chunk(m, n, chunks)] * chunks == [256] * chunks
     ref = oracle.gemm(qa, sa[1], 1, qb, sb[1], 1)
     _assert_close(c_ovl, ref, _abs_sum_full(qa, sa[1], 1, qb, sb[1], 1), f"split ring overlapped k={k}")
+
+
+@pytest.mark.parametrize("kt", list(range(2, 14)))
+def test_gemm_two_group_kernel_every_last_step(kt):
+    """The two-group kernel runs its K loop six steps at a time (two A slots, three B slots and
+    two scale register sets in turn) and leaves it after whichever step is the last: for 2 to
+    13 K steps it gives the bits of the split ring with the plain epilogue, each run after a
+    decoy product on other operands (LDS read before its load landed would hold the decoy's
+    data)."""
+    m, n, chunks, k = 3968, 8000, 2, 128 * kt
+    print(f"two-group kernel k={k}", flush=True)
+    qa, sa, qb, sb = _operands(m, n, k, seed_a=kt + 40, seed_b=kt + 41)
+    xa, xsa, xb, xsb = _operands(m, n, k, seed_a=kt + 42, seed_b=kt + 43)
+    _gpu_gemm(xa, xsa[1], 1, xb, xsb[1], 1, num_chunks=chunks, first_chunk=1, pad_cols=8)
+    c_two = _gpu_gemm(qa, sa[1], 1, qb, sb[1], 1, num_chunks=chunks, first_chunk=1, pad_cols=8)
+    _gpu_gemm(xa, xsa[1], 1, xb, xsb[1], 1, num_chunks=chunks, first_chunk=1, pad_cols=4)
+    c_plain = _gpu_gemm(qa, sa[1], 1, qb, sb[1], 1, num_chunks=chunks, first_chunk=1, pad_cols=4)
+    assert np.array_equal(c_two, c_plain), f"k={k}"
+    if kt == 7:
+        ref = oracle.gemm(qa, sa[1], 1, qb, sb[1], 1)
+        _assert_close(c_two, ref, _abs_sum_full(qa, sa[1], 1, qb, sb[1], 1), f"two-group k={k}")
 
 
 @pytest.mark.parametrize("m,n,k,chunks", [(64, 1, 128, 1), (33, 17, 256, 1), (200, 40, 16384, 2),
@@ -434,7 +456,7 @@ def test_gemm_wide_scale_range_closed_form():
 
 
 def test_gemm_wide_scale_range_split_ring():
-    """The same on the 256 x 256 split-ring kernel (swizzled, 16-byte aligned scales in
+    """The same on the 256 x 256 two-group kernel (swizzled, 16-byte aligned scales in
     registers), compared on sampled outputs."""
     m, n, k, chunks = 4096, 4096, 512, 4
     assert mx.gemm_tiles_per_chunk(m, n, chunks) == 4 * 16
