@@ -680,9 +680,10 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
 //    so that every slot offset is a constant.
 //  * A load instruction can take hundreds of cycles to issue when the memory pipeline is busy,
 //    so the loads are issued in the memory phases, after the fragment reads.
-//  * Per step and wave the loads leave in one order (scales of step s + 1, A(s + 1), B(s + 2)),
-//    so that two fixed counts wait for B(s + 1) before the last barrier that precedes its first
-//    read and for A(s + 1) before the group's own first read. Loads past the last step go
+//  * Per step and wave the loads leave in one order (A scales of step s + 1, A(s + 1), then
+//    B(s + 2), B scales of step s + 1: five per memory phase), so that two fixed counts wait
+//    for B(s + 1) before the last barrier that precedes its first read and for A(s + 1) before
+//    the group's own first read. Loads past the last step go
 //    through empty resources (dropped) so that the counts hold on every path.
 //  * After the last step of a tile the workgroup issues the next tile's B(0), scales, A(0) and
 //    B(1) (A slot 0, B slots 0 and 1), then writes the BF16 tile out in four quarters of
@@ -787,10 +788,14 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(st + (wave * T::DB + i) * 1024), 16, ts.b_off[i],
                                                (uint32_t)kt * BK, 0, 0);
   };
-  auto load_scales = [&](const TileState& ts, int kt, u32x2& sa, u32x4& sb) {
+  auto load_sa = [&](const TileState& ts, int kt, u32x2& sa) {
     const bool live = kt < KT;
     const int so = live ? kt * (int)scale_step<1>() : 0;
     sa = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(make_rsrc(As, live ? sa_bytes : 0u), ts.sa_off, so, 0));
+  };
+  auto load_sb = [&](const TileState& ts, int kt, u32x4& sb) {
+    const bool live = kt < KT;
+    const int so = live ? kt * (int)scale_step<1>() : 0;
     sb = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(Bs, live ? sb_bytes : 0u), ts.sb_off, so, 0));
   };
   // a tile's first loads, in the loop's order (B(s + 1) issued last before step s), so that the
@@ -798,11 +803,13 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
   auto first_loads = [&](const TileState& ts, u32x2& sa, u32x4& sb) {
     issue_b(ts, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    load_scales(ts, 0, sa, sb);
+    load_sa(ts, 0, sa);
     __builtin_amdgcn_sched_barrier(0);
     issue_a(ts, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
     issue_b(ts, 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_sb(ts, 0, sb);
     __builtin_amdgcn_sched_barrier(0);
   };
   // end of a phase: nothing moves across it, and every wave's LDS reads have completed
@@ -877,13 +884,14 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
         bf[t] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
     };
-    // the half step's MFMAs; scale byte 0 (first 64 K) or 2 (second 64 K) of this lane's block g
+    // the half step's MFMAs: the instruction takes byte 0 (first 64 K) or 2 (second 64 K) of
+    // each scale register, so lanes of block g = 1 shift theirs down by one byte
     auto mma_half = [&](int ks, const v8i (&af)[T::TM], const v8i (&bf)[T::TN], const u32x2& sa, const u32x4& sb) {
       uint32_t as_sel[T::TM], bs_sel[T::TN];
 #pragma unroll
-      for (int t = 0; t < T::TM; ++t) as_sel[t] = (sa[t] >> (8 * g)) & 0x00FF00FFu;
+      for (int t = 0; t < T::TM; ++t) as_sel[t] = sa[t] >> (8 * g);
 #pragma unroll
-      for (int t = 0; t < T::TN; ++t) bs_sel[t] = (sb[t] >> (8 * g)) & 0x00FF00FFu;
+      for (int t = 0; t < T::TN; ++t) bs_sel[t] = sb[t] >> (8 * g);
 #pragma unroll
       for (int x = 0; x < T::TN; ++x)
 #pragma unroll
@@ -895,10 +903,11 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
         }
     };
     // One 128-K step s (J = s mod 6) as four phases. First memory phase: the fragments, then the
-    // scales of step s + 1 and A(s + 1) (into this group's rows of the slot of step s - 1, which
-    // the group has finished reading). Second memory phase: the fragments, then B(s + 2) (into
-    // the slot of step s - 1, which both groups have finished reading). In a tile's first step
-    // the previous tile's 16 C stores may still be in flight behind B(1).
+    // A scales of step s + 1 and A(s + 1) (into this group's rows of the slot of step s - 1,
+    // which the group has finished reading). Second memory phase: the fragments, then B(s + 2)
+    // (into the slot of step s - 1, which both groups have finished reading) and the B scales of
+    // step s + 1. In a tile's first step the previous tile's 16 C stores may still be in flight
+    // behind B(1) and the B scales of step 0.
     auto stage = [&](auto Jc, int s, auto First) {
       constexpr int J = decltype(Jc)::value;
       constexpr bool FIRST = decltype(First)::value;
@@ -907,7 +916,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
       // memory, first half
       read_frags(AS, BS, 0, af, bf);
       __builtin_amdgcn_sched_barrier(0);
-      load_scales(cur, s + 1, sa2[NXT], sb2[NXT]);
+      load_sa(cur, s + 1, sa2[NXT]);
       __builtin_amdgcn_sched_barrier(0);
       issue_a(cur, s + 1, AS ^ 1);
       phase_end();
@@ -916,29 +925,33 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
       mma_half(0, af, bf, sa2[CUR], sb2[CUR]);
       __builtin_amdgcn_s_setprio(0);
       phase_end();
-      // memory, second half; then B(s + 1) has landed (behind it: the scales of s + 1, A(s + 1)
-      // and B(s + 2)), before the barrier after which the first group reads it
+      // memory, second half; then B(s + 1) has landed (behind it: the B scales of s, the A
+      // scales of s + 1, A(s + 1), B(s + 2) and the B scales of s + 1), before the barrier after
+      // which the first group reads it
       read_frags(AS, BS, 1, af, bf);
       __builtin_amdgcn_sched_barrier(0);
       issue_b(cur, s + 2, (J + 2) % 3);
       __builtin_amdgcn_sched_barrier(0);
+      load_sb(cur, s + 1, sb2[NXT]);
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (FIRST)
-        wait_vm<C_STORES + 2 + T::DA + T::DB>();
+        wait_vm<C_STORES + 3 + T::DA + T::DB>();
       else
-        wait_vm<2 + T::DA + T::DB>();
+        wait_vm<3 + T::DA + T::DB>();
       phase_end();
-      // compute, second half; then A(s + 1) has landed (behind it: B(s + 2)), before the barrier
-      // after which this group reads it
+      // compute, second half; then A(s + 1) has landed (behind it: B(s + 2) and the B scales of
+      // s + 1), before the barrier after which this group reads it
       __builtin_amdgcn_s_setprio(1);
       mma_half(1, af, bf, sa2[CUR], sb2[CUR]);
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm<T::DB>();
+      wait_vm<T::DB + 1>();
       phase_end();
     };
-    // B(0), the scales of step 0 and A(0) have landed; B(1) and the 16 C stores issued after it
-    // (the previous tile's, or before the first tile 16 dropped ones) may still be in flight
-    wait_vm<T::DB + C_STORES>();
+    // B(0), the A scales of step 0 and A(0) have landed; B(1), the B scales of step 0 and the 16
+    // C stores issued after them (the previous tile's, or before the first tile 16 dropped
+    // ones) may still be in flight
+    wait_vm<T::DB + 1 + C_STORES>();
     phase_end();
     if (grp) phase_end();  // the second group starts one phase late
     // The first step on its own (its count lets the previous tile's C stores stay in flight),
