@@ -663,11 +663,10 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
   }
 }
 
-// Tile configurations: output tile, wave grid, LDS stages.
-// BF16-output GEMM on 256 x 256 tiles whose eight waves take turns on the matrix pipes. Waves
-// 0-3 (tile rows 0-127) and waves 4-7 (rows 128-255) put one wave of each group on every SIMD.
-// Each wave alternates a memory phase (the LDS fragment reads of one 64-K half step into
-// registers, then its share of the loads) and a compute phase (the half step's eight scaled
+// BF16-output GEMM on 256 x 256 or 256 x 192 tiles whose eight waves take turns on the matrix
+// pipes. Waves 0-3 (tile rows 0-127) and waves 4-7 (rows 128-255) put one wave of each group on
+// every SIMD. Each wave alternates a memory phase (the LDS fragment reads of one 64-K half step
+// into registers, then its share of the loads) and a compute phase (the half step's scaled
 // MFMAs from those registers), with a workgroup barrier after every phase; the second group
 // starts one phase late, so that on each SIMD one wave issues MFMAs while the other reads its
 // next fragments. B is in a ring of three LDS slots (fetched two steps ahead) and A in two (one
@@ -681,29 +680,38 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
 //  * A load instruction can take hundreds of cycles to issue when the memory pipeline is busy,
 //    so the loads are issued in the memory phases, after the fragment reads.
 //  * Per step and wave the loads leave in one order (A scales of step s + 1, A(s + 1), then
-//    B(s + 2), B scales of step s + 1: five per memory phase), so that two fixed counts wait
-//    for B(s + 1) before the last barrier that precedes its first read and for A(s + 1) before
-//    the group's own first read. Loads past the last step go
-//    through empty resources (dropped) so that the counts hold on every path.
-//  * After the last step of a tile the workgroup issues the next tile's B(0), scales, A(0) and
-//    B(1) (A slot 0, B slots 0 and 1), then writes the BF16 tile out in four quarters of
-//    128 rows x 128 columns staged alternately in A slot 1 and B slot 2. The C stores are
-//    buffer stores over the tile's own rows (elements past the last row or column are dropped),
-//    so every wave issues the same 16 stores, and the next tile's first waits let exactly those
-//    stay in flight.
+//    B(s + 2), B scales of step s + 1), so that two fixed counts wait for B(s + 1) before the
+//    last barrier that precedes its first read and for A(s + 1) before the group's own first
+//    read. Loads past the last step go through empty resources (dropped) so that the counts
+//    hold on every path.
+//  * 256 x 256: after the last step of a tile the workgroup issues the next tile's B(0),
+//    scales, A(0) and B(1) (A slot 0, B slots 0 and 1), then writes the BF16 tile out in four
+//    quarters of 128 rows x 128 columns staged alternately in A slot 1 and B slot 2. The C
+//    stores are buffer stores over the tile's own rows (elements past the last row or column
+//    are dropped), so every wave issues the same 16 stores, and the next tile's first waits let
+//    exactly those stay in flight. 256 x 192 (two tiles per compute unit at most, for the
+//    M = 2048-4096 workloads): the whole tile is staged once the loads have landed.
 template <class T>
 __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, uint16_t* __restrict__ C, int M, int N, int K, int ldc, int num_chunks,
     int first_chunk, int* __restrict__ chunk_done) {
-  static_assert(T::SPLIT && T::BM == 256 && T::BN == 256 && T::TM == 2 && T::TN == 4 && T::NT == 512 &&
-                    T::DA == 4 && T::DB == 4 && T::WTM == 64 && T::WTN == 128 && T::B_BYTES == 32768 &&
-                    T::A_BYTES == 32768,
-                "256 x 256 tiles of 8 waves of 64 x 128");
   constexpr int BM = T::BM, BN = T::BN;
-  // B slots at 0, 32 and 64 KiB, A slots at 96 and 128 KiB
+  static_assert(T::SPLIT && BM == 256 && (BN == 256 || BN == 192) && T::TM == 2 && T::NT == 512 &&
+                    T::DA == 4 && T::WTM == 64 && T::A_BYTES == 32768 && T::WTN == BN / 2,
+                "256-row tiles of 8 waves of 64 x BN/2");
+  constexpr int TN = T::TN;
+  // overlapped epilogue (quarters through A slot 1 and B slot 2): 256 x 256
+  constexpr bool OVL = BN == 256;
+  // B slots at 0, 1 and 2 B_BYTES, A slots after them
   constexpr int B_RING = 0, A_RING = 3 * T::B_BYTES;
-  constexpr int C_STORES = 16;  // C stores per thread and tile
+  static_assert(A_RING + 2 * T::A_BYTES <= 160 * 1024, "ring");
+  // B slot 2 lies beyond the 64 KiB reach of an instruction offset from the slot-0 base
+  constexpr bool FAR_B2 = 2 * T::B_BYTES + (TN - 1) * 32 * 128 + 32 * 128 > 65536;
+  // B scale loads per step: one 16-byte load of the wave's four row blocks (256 x 256, where
+  // they are one swizzled 128-row group), else one per row block
+  constexpr int NSB = BN == 256 ? 1 : TN;
+  constexpr int C_STORES = OVL ? 16 : 0;  // C stores per thread and tile left in flight
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
 #if defined(__HIP_DEVICE_COMPILE__)
   const int tid = threadIdx.x;
@@ -724,14 +732,14 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
   const uint32_t sa_bytes = (uint32_t)((M + 127) / 128 * 128) * nblk4 * 4;
   const uint32_t sb_bytes = (uint32_t)((N + 127) / 128 * 128) * nblk4 * 4;
   const uint32_t a_bytes = (uint32_t)M * (uint32_t)K, b_bytes = (uint32_t)N * (uint32_t)K;
-  // epilogue staging: A slot 1 and B slot 2 (the next tile's first loads use the other slots)
+  // overlapped epilogue staging: A slot 1 and B slot 2 (the next tile's first loads use the others)
   uint8_t* const stage0 = smem + A_RING + T::A_BYTES;
   uint8_t* const stage1 = smem + B_RING + 2 * T::B_BYTES;
 
   // ---- per-tile state: output origin and the offsets of its loads
   struct TileState {
     int m0, m_end, n0, chunk;
-    uint32_t a_off[T::DA], b_off[T::DB], sa_off, sb_off;
+    uint32_t a_off[T::DA], b_off[T::DB], sa_off, sb_off[NSB];
   };
   auto setup = [&](int bid, TileState& ts) {
     const int ci = bid / tpc;
@@ -766,10 +774,13 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
       ts.b_off[i] = (uint32_t)min(ts.n0 + r, N - 1) * (uint32_t)K + (((sidx & 7) ^ swz(r)) * 16);
     }
     // rows r, r + 32, r + 64, r + 96 of a swizzled 128-row group keep their 4-byte scale groups
-    // side by side: one 8-byte load for the wave's two A row blocks, one 16-byte load for its
-    // four B row blocks (rows past the operand read zero padding or 0; not stored)
+    // side by side: one 8-byte load for the wave's two A row blocks, one 16-byte load for the
+    // four B row blocks of a 128-column wave, one 4-byte load per block otherwise (rows past the
+    // operand read zero padding or 0; not stored)
     ts.sa_off = scale_base<1>((uint32_t)(ts.m0 + wm * T::WTM + (ln & 31)), nblk4);
-    ts.sb_off = scale_base<1>((uint32_t)(ts.n0 + wn * T::WTN + (ln & 31)), nblk4);
+#pragma unroll
+    for (int t = 0; t < NSB; ++t)
+      ts.sb_off[t] = scale_base<1>((uint32_t)(ts.n0 + wn * T::WTN + 32 * t + (ln & 31)), nblk4);
   };
   // loads past the last step go through empty resources: dropped, but counted like the others
   auto issue_a = [&](const TileState& ts, int kt, int slot) {
@@ -788,28 +799,42 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(st + (wave * T::DB + i) * 1024), 16, ts.b_off[i],
                                                (uint32_t)kt * BK, 0, 0);
   };
-  auto load_sa = [&](const TileState& ts, int kt, u32x2& sa) {
+  // scale registers of one step: the wave's A row blocks, then its B row blocks
+  struct Scales {
+    u32x2 a;
+    uint32_t b[TN];
+  };
+  auto load_sa = [&](const TileState& ts, int kt, Scales& sc) {
     const bool live = kt < KT;
     const int so = live ? kt * (int)scale_step<1>() : 0;
-    sa = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(make_rsrc(As, live ? sa_bytes : 0u), ts.sa_off, so, 0));
+    sc.a = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(make_rsrc(As, live ? sa_bytes : 0u), ts.sa_off, so, 0));
   };
-  auto load_sb = [&](const TileState& ts, int kt, u32x4& sb) {
+  auto load_sb = [&](const TileState& ts, int kt, Scales& sc) {
     const bool live = kt < KT;
     const int so = live ? kt * (int)scale_step<1>() : 0;
-    sb = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(Bs, live ? sb_bytes : 0u), ts.sb_off, so, 0));
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(Bs, live ? sb_bytes : 0u);
+    if constexpr (NSB == 1) {
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ts.sb_off[0], so, 0));
+#pragma unroll
+      for (int t = 0; t < TN; ++t) sc.b[t] = v[t];
+    } else {
+#pragma unroll
+      for (int t = 0; t < TN; ++t) sc.b[t] = __builtin_amdgcn_raw_buffer_load_b32(r, ts.sb_off[t], so, 0);
+    }
   };
-  // a tile's first loads, in the loop's order (B(s + 1) issued last before step s), so that the
-  // counts and the compiler's own waits for the scales see the same loads in flight
-  auto first_loads = [&](const TileState& ts, u32x2& sa, u32x4& sb) {
+  // a tile's first loads, in the loop's order (B(s + 1) and the B scales issued last before
+  // step s), so that the counts and the compiler's own waits for the scales see the same loads
+  // in flight
+  auto first_loads = [&](const TileState& ts, Scales& sc) {
     issue_b(ts, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    load_sa(ts, 0, sa);
+    load_sa(ts, 0, sc);
     __builtin_amdgcn_sched_barrier(0);
     issue_a(ts, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
     issue_b(ts, 1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    load_sb(ts, 0, sb);
+    load_sb(ts, 0, sc);
     __builtin_amdgcn_sched_barrier(0);
   };
   // end of a phase: nothing moves across it, and every wave's LDS reads have completed
@@ -823,10 +848,9 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
   if (bid >= total) return;
   TileState cur;
   setup(bid, cur);
-  u32x2 sa2[2];
-  u32x4 sb2[2];
-  first_loads(cur, sa2[0], sb2[0]);
-  {
+  Scales sc2[2];
+  first_loads(cur, sc2[0]);
+  if constexpr (OVL) {
     // 16 stores past the end of an empty resource (dropped): every tile then starts with the
     // same 16 stores behind its first loads. They must stay behind those loads: the compiler
     // may otherwise interleave them, and the first counts would no longer cover the loads.
@@ -838,9 +862,10 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
   }
 
   while (true) {
-    // per-lane LDS bases of the fragment reads: A slot 0 (slot 1 at +32 KiB), B slots 0 and 1
-    // (+32 KiB) and B slot 2; the block offsets t * 4 KiB and the slot offsets are instruction
-    // offsets (below 64 KiB). From an opaque copy of the lane index, per tile.
+    // per-lane LDS bases of the fragment reads: A slot 0 (slot 1 at +32 KiB), B slot 0 (slots
+    // 1 and 2 at + B_BYTES and + 2 B_BYTES, or slot 2 from a base of its own when it lies beyond
+    // the reach of an instruction offset); the block offsets t * 4 KiB and the slot offsets are
+    // instruction offsets (below 64 KiB). From an opaque copy of the lane index, per tile.
     int va[2][2], vb[2][2], vb2[2][2];
     {
       int ln = lane;
@@ -854,19 +879,22 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
           va[kk][h] = A_RING + wm * T::WTM * 128 + oa[kk][h];
           vb[kk][h] = B_RING + wn * T::WTN * 128 + ob[kk][h];
           vb2[kk][h] = vb[kk][h] + 2 * T::B_BYTES;
-          asm volatile("" : "+v"(va[kk][h]), "+v"(vb[kk][h]), "+v"(vb2[kk][h]));
+          if constexpr (FAR_B2)
+            asm volatile("" : "+v"(va[kk][h]), "+v"(vb[kk][h]), "+v"(vb2[kk][h]));
+          else
+            asm volatile("" : "+v"(va[kk][h]), "+v"(vb[kk][h]));
         }
     }
-    v16f acc[T::TN][T::TM];
+    v16f acc[TN][T::TM];
 #pragma unroll
-    for (int x = 0; x < T::TN; ++x)
+    for (int x = 0; x < TN; ++x)
 #pragma unroll
       for (int y = 0; y < T::TM; ++y)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[x][y][v] = 0.f;
 
     // fragments of one 64-K half step (ks) from A slot sa_slot and B slot sb_slot
-    auto read_frags = [&](int sa_slot, int sb_slot, int ks, v8i (&af)[T::TM], v8i (&bf)[T::TN]) {
+    auto read_frags = [&](int sa_slot, int sb_slot, int ks, v8i (&af)[T::TM], v8i (&bf)[TN]) {
 #pragma unroll
       for (int t = 0; t < T::TM; ++t) {
         const int kk = ks ^ (t & 1);
@@ -876,24 +904,24 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
         af[t] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
 #pragma unroll
-      for (int t = 0; t < T::TN; ++t) {
+      for (int t = 0; t < TN; ++t) {
         const int kk = ks ^ (t & 1);
-        const int b0 = sb_slot == 2 ? vb2[kk][0] : vb[kk][0] + sb_slot * T::B_BYTES;
-        const int b1 = sb_slot == 2 ? vb2[kk][1] : vb[kk][1] + sb_slot * T::B_BYTES;
+        const int b0 = FAR_B2 && sb_slot == 2 ? vb2[kk][0] : vb[kk][0] + sb_slot * T::B_BYTES;
+        const int b1 = FAR_B2 && sb_slot == 2 ? vb2[kk][1] : vb[kk][1] + sb_slot * T::B_BYTES;
         const v4i lo = *(const v4i*)(smem + b0 + t * 32 * 128), hi = *(const v4i*)(smem + b1 + t * 32 * 128);
         bf[t] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
     };
     // the half step's MFMAs: the instruction takes byte 0 (first 64 K) or 2 (second 64 K) of
     // each scale register, so lanes of block g = 1 shift theirs down by one byte
-    auto mma_half = [&](int ks, const v8i (&af)[T::TM], const v8i (&bf)[T::TN], const u32x2& sa, const u32x4& sb) {
-      uint32_t as_sel[T::TM], bs_sel[T::TN];
+    auto mma_half = [&](int ks, const v8i (&af)[T::TM], const v8i (&bf)[TN], const Scales& sc) {
+      uint32_t as_sel[T::TM], bs_sel[TN];
 #pragma unroll
-      for (int t = 0; t < T::TM; ++t) as_sel[t] = sa[t] >> (8 * g);
+      for (int t = 0; t < T::TM; ++t) as_sel[t] = sc.a[t] >> (8 * g);
 #pragma unroll
-      for (int t = 0; t < T::TN; ++t) bs_sel[t] = sb[t] >> (8 * g);
+      for (int t = 0; t < TN; ++t) bs_sel[t] = sc.b[t] >> (8 * g);
 #pragma unroll
-      for (int x = 0; x < T::TN; ++x)
+      for (int x = 0; x < TN; ++x)
 #pragma unroll
         for (int y = 0; y < T::TM; ++y) {
           if (ks == 0)
@@ -906,23 +934,23 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     // A scales of step s + 1 and A(s + 1) (into this group's rows of the slot of step s - 1,
     // which the group has finished reading). Second memory phase: the fragments, then B(s + 2)
     // (into the slot of step s - 1, which both groups have finished reading) and the B scales of
-    // step s + 1. In a tile's first step the previous tile's 16 C stores may still be in flight
+    // step s + 1. In a tile's first step the previous tile's C stores may still be in flight
     // behind B(1) and the B scales of step 0.
     auto stage = [&](auto Jc, int s, auto First) {
       constexpr int J = decltype(Jc)::value;
       constexpr bool FIRST = decltype(First)::value;
       constexpr int AS = J & 1, BS = J % 3, CUR = J & 1, NXT = (J + 1) & 1;
-      v8i af[T::TM], bf[T::TN];
+      v8i af[T::TM], bf[TN];
       // memory, first half
       read_frags(AS, BS, 0, af, bf);
       __builtin_amdgcn_sched_barrier(0);
-      load_sa(cur, s + 1, sa2[NXT]);
+      load_sa(cur, s + 1, sc2[NXT]);
       __builtin_amdgcn_sched_barrier(0);
       issue_a(cur, s + 1, AS ^ 1);
       phase_end();
       // compute, first half
       __builtin_amdgcn_s_setprio(1);
-      mma_half(0, af, bf, sa2[CUR], sb2[CUR]);
+      mma_half(0, af, bf, sc2[CUR]);
       __builtin_amdgcn_s_setprio(0);
       phase_end();
       // memory, second half; then B(s + 1) has landed (behind it: the B scales of s, the A
@@ -932,26 +960,27 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
       __builtin_amdgcn_sched_barrier(0);
       issue_b(cur, s + 2, (J + 2) % 3);
       __builtin_amdgcn_sched_barrier(0);
-      load_sb(cur, s + 1, sb2[NXT]);
+      load_sb(cur, s + 1, sc2[NXT]);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (FIRST)
-        wait_vm<C_STORES + 3 + T::DA + T::DB>();
+        wait_vm<C_STORES + 2 * NSB + 1 + T::DA + T::DB>();
       else
-        wait_vm<3 + T::DA + T::DB>();
+        wait_vm<2 * NSB + 1 + T::DA + T::DB>();
       phase_end();
       // compute, second half; then A(s + 1) has landed (behind it: B(s + 2) and the B scales of
       // s + 1), before the barrier after which this group reads it
       __builtin_amdgcn_s_setprio(1);
-      mma_half(1, af, bf, sa2[CUR], sb2[CUR]);
+      mma_half(1, af, bf, sc2[CUR]);
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm<T::DB + 1>();
+      wait_vm<T::DB + NSB>();
       phase_end();
     };
-    // B(0), the A scales of step 0 and A(0) have landed; B(1), the B scales of step 0 and the 16
-    // C stores issued after them (the previous tile's, or before the first tile 16 dropped
-    // ones) may still be in flight
-    wait_vm<T::DB + 1 + C_STORES>();
+
+    // B(0), the A scales of step 0 and A(0) have landed; B(1), the B scales of step 0 and the C
+    // stores issued after them (the previous tile's, or before the first tile dropped ones) may
+    // still be in flight
+    wait_vm<T::DB + NSB + C_STORES>();
     phase_end();
     if (grp) phase_end();  // the second group starts one phase late
     // The first step on its own (its count lets the previous tile's C stores stay in flight),
@@ -979,71 +1008,112 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     wait_vm<0>();           // the dropped loads too: nothing writes LDS under the epilogue
     // the scale registers stay live past the loop: otherwise the compiler sinks each step's scale
     // loads into the next step (their only use, behind an early exit), right before the MFMAs
-    asm volatile("" ::"v"(sa2[0]), "v"(sa2[1]), "v"(sb2[0]), "v"(sb2[1]));
+    asm volatile("" ::"v"(sc2[0].a), "v"(sc2[1].a));
+#pragma unroll
+    for (int t = 0; t < TN; ++t) asm volatile("" ::"v"(sc2[0].b[t]), "v"(sc2[1].b[t]));
 
-    // ---- epilogue, with the next tile's first loads issued half-way
     block_barrier();  // every wave's loads have landed and its reads are done
     int tid_e = tid;
     asm volatile("" : "+v"(tid_e));
     const int e32 = tid_e & 31, eg = (tid_e >> 5) & 1;
-    // Quarter qd = (y, h): tile rows 64 wm + 32 y + [0, 32) of every wm and tile columns
-    // 128 wn + 64 h + [0, 64) of both wn, staged as 128 rows of 256 bytes (row 32 wm + l32,
-    // 16-byte chunk 8 wn + column / 8 within the half) with the chunk index xor-ed with row & 7,
-    // so that the 8-byte writes (32 rows) and the 16-byte reads (4 whole rows) of one
-    // instruction both spread evenly over the banks.
-    auto stage_quarter = [&](int qd, uint8_t* st) {
-      const int y = qd >> 1, h = qd & 1;
-      const int rq = wm * 32 + e32;
-#pragma unroll
-      for (int xx = 0; xx < 2; ++xx) {
-        const int x = 2 * h + xx;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int chunk = wn * 8 + xx * 4 + q;
-          const uint32_t lo = pack_bf16x2(acc[x][y][4 * q + 0], acc[x][y][4 * q + 1]);
-          const uint32_t hi = pack_bf16x2(acc[x][y][4 * q + 2], acc[x][y][4 * q + 3]);
-          *(uint2*)(st + rq * 256 + ((chunk ^ (rq & 7)) * 16) + eg * 8) = make_uint2(lo, hi);
-        }
-      }
-    };
-    // the first two quarters (half of the accumulators) go to LDS before the next tile's loads
-    // are issued, so that its offsets and this tile's remaining accumulators fit
-    stage_quarter(0, stage0);
-    stage_quarter(1, stage1);
     const TileState done = cur;
     const int nbid = bid + (int)gridDim.x;
     const bool has_next = nbid < total;
-    if (has_next) {
-      setup(nbid, cur);
-      first_loads(cur, sa2[0], sb2[0]);
-    }
-    // C through a resource over this tile's rows: elements past the last row or column get an
-    // offset past its end and are dropped, so every wave issues the same 16 stores
-    const uint32_t c_bytes = (uint32_t)(done.m_end - done.m0) * (uint32_t)ldc * 2u;
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(C + (int64_t)done.m0 * ldc, c_bytes);
-    auto store_quarter = [&](int qd, const uint8_t* st) {
-      const int y = qd >> 1, h = qd & 1;
+    if constexpr (OVL) {
+      // ---- epilogue, with the next tile's first loads issued half-way.
+      // Quarter qd = (y, h): tile rows 64 wm + 32 y + [0, 32) of every wm and tile columns
+      // 128 wn + 64 h + [0, 64) of both wn, staged as 128 rows of 256 bytes (row 32 wm + l32,
+      // 16-byte chunk 8 wn + column / 8 within the half) with the chunk index xor-ed with
+      // row & 7, so that the 8-byte writes (32 rows) and the 16-byte reads (4 whole rows) of one
+      // instruction both spread evenly over the banks.
+      auto stage_quarter = [&](int qd, uint8_t* st) {
+        const int y = qd >> 1, h = qd & 1;
+        const int rq = wm * 32 + e32;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = tid_e + i * T::NT;
-        const int rq = p >> 4, chunk = p & 15;
-        const u32x4 v = *(const u32x4*)(st + rq * 256 + ((chunk ^ (rq & 7)) * 16));
-        const int r = (rq >> 5) * 64 + y * 32 + (rq & 31);  // tile row
-        const int n = done.n0 + (chunk >> 3) * 128 + h * 64 + (chunk & 7) * 8;
-        const bool ok = done.m0 + r < done.m_end && n < N;
-        const uint32_t off = ok ? ((uint32_t)r * (uint32_t)ldc + (uint32_t)n) * 2u : 0x80000000u;
-        __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 2);
+        for (int xx = 0; xx < 2; ++xx) {
+          const int x = 2 * h + xx;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int chunk = wn * 8 + xx * 4 + q;
+            const uint32_t lo = pack_bf16x2(acc[x][y][4 * q + 0], acc[x][y][4 * q + 1]);
+            const uint32_t hi = pack_bf16x2(acc[x][y][4 * q + 2], acc[x][y][4 * q + 3]);
+            *(uint2*)(st + rq * 256 + ((chunk ^ (rq & 7)) * 16) + eg * 8) = make_uint2(lo, hi);
+          }
+        }
+      };
+      // the first two quarters (half of the accumulators) go to LDS before the next tile's
+      // loads are issued, so that its offsets and this tile's remaining accumulators fit
+      stage_quarter(0, stage0);
+      stage_quarter(1, stage1);
+      if (has_next) {
+        setup(nbid, cur);
+        first_loads(cur, sc2[0]);
       }
-    };
-    block_barrier();
-    store_quarter(0, stage0);
-    store_quarter(1, stage1);
-    block_barrier();
-    stage_quarter(2, stage0);
-    stage_quarter(3, stage1);
-    block_barrier();
-    store_quarter(2, stage0);
-    store_quarter(3, stage1);
+      // C through a resource over this tile's rows: elements past the last row or column get
+      // an offset past its end and are dropped, so every wave issues the same 16 stores
+      const uint32_t c_bytes = (uint32_t)(done.m_end - done.m0) * (uint32_t)ldc * 2u;
+      const __amdgpu_buffer_rsrc_t rc = make_rsrc(C + (int64_t)done.m0 * ldc, c_bytes);
+      auto store_quarter = [&](int qd, const uint8_t* st) {
+        const int y = qd >> 1, h = qd & 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int p = tid_e + i * T::NT;
+          const int rq = p >> 4, chunk = p & 15;
+          const u32x4 v = *(const u32x4*)(st + rq * 256 + ((chunk ^ (rq & 7)) * 16));
+          const int r = (rq >> 5) * 64 + y * 32 + (rq & 31);  // tile row
+          const int n = done.n0 + (chunk >> 3) * 128 + h * 64 + (chunk & 7) * 8;
+          const bool ok = done.m0 + r < done.m_end && n < N;
+          const uint32_t off = ok ? ((uint32_t)r * (uint32_t)ldc + (uint32_t)n) * 2u : 0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 2);
+        }
+      };
+      block_barrier();
+      store_quarter(0, stage0);
+      store_quarter(1, stage1);
+      block_barrier();
+      stage_quarter(2, stage0);
+      stage_quarter(3, stage1);
+      block_barrier();
+      store_quarter(2, stage0);
+      store_quarter(3, stage1);
+    } else {
+      // ---- epilogue: the BF16 tile staged in LDS (rows padded by 16 bytes, 8-byte halves
+      // swapped on alternate row groups), then full-line 16-byte stores; the next tile's first
+      // loads once every wave has read its part
+#pragma unroll
+      for (int x = 0; x < TN; ++x) {
+#pragma unroll
+        for (int y = 0; y < T::TM; ++y) {
+          const int r = wm * T::WTM + y * 32 + e32;
+          const int gs = eg ^ (((r >> 3) ^ (r >> 4)) & 1);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int c = wn * T::WTN + x * 32 + 8 * q + 4 * gs;
+            const uint32_t lo = pack_bf16x2(acc[x][y][4 * q + 0], acc[x][y][4 * q + 1]);
+            const uint32_t hi = pack_bf16x2(acc[x][y][4 * q + 2], acc[x][y][4 * q + 3]);
+            *(uint2*)(smem + r * T::C_STRIDE + c * 2) = make_uint2(lo, hi);
+          }
+        }
+      }
+      block_barrier();
+      constexpr int SEGS = BN / 8;  // 16-byte segments per row
+#pragma unroll 4
+      for (int p = tid_e; p < BM * SEGS; p += T::NT) {
+        const int r = p / SEGS;
+        const int c8 = (p % SEGS) * 8;
+        const int m = done.m0 + r;
+        const int n = done.n0 + c8;
+        if (m >= done.m_end || n >= N) continue;
+        uint4 v = *(const uint4*)(smem + r * T::C_STRIDE + c8 * 2);
+        if (((r >> 3) ^ (r >> 4)) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+        __builtin_nontemporal_store(*(const u32x4*)&v, (u32x4*)(C + (int64_t)m * ldc + n));
+      }
+      if (has_next) {
+        block_barrier();  // every wave has read its part of the staged tile
+        setup(nbid, cur);
+        first_loads(cur, sc2[0]);
+      }
+    }
 
     if (chunk_done != nullptr) {
       __threadfence();  // this thread's C stores are visible device-wide
@@ -1056,9 +1126,11 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
 #endif
 }
 
+// Tile configurations: output tile, wave grid, LDS stages.
 using TileL = Tile<256, 256, 4, 2, 2>;  // 8 waves of 64 x 128; large problems
 using TileLR = Tile<256, 256, 4, 2, 2, true>;  // the same with the split ring (swizzled scales)
 using TileN = Tile<256, 192, 4, 2, 2>;  // 8 waves of 64 x 96; when 256 x 256 leaves a round part-empty
+using TileNR = Tile<256, 192, 4, 2, 2, true>;  // the same as two wave groups (swizzled scales)
 using TileW = Tile<128, 192, 4, 2, 3>;  // 8 waves of 32 x 96
 using TileQ = Tile<192, 192, 3, 2, 3>;  // 6 waves of 64 x 96
 using TileR = Tile<96, 192, 3, 2, 4>;   // 6 waves of 32 x 96
@@ -1160,6 +1232,23 @@ bool split_ring_fits(const uint8_t* as, int a_layout, const uint8_t* bs, int b_l
          (num_chunks == 1 || (m / num_chunks) % 64 == 0);
 }
 
+// The two-group BF16 kernel (swizzled, 16-byte aligned scales on 64-row chunk boundaries, checked
+// by the caller): output in whole 16-byte segments, at least two K steps, tile offsets in 32
+// bits. Returns false (launching nothing) when the output does not qualify.
+template <class T>
+bool launch_two_group(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs, int64_t m, int64_t n,
+                      int64_t k, uint16_t* c, int64_t ldc, int num_chunks, int first_chunk, int* chunk_done,
+                      hipStream_t stream, hipError_t& err) {
+  const bool wide = (uintptr_t)c % 16 == 0 && ldc % 8 == 0;
+  if (!(k >= 2 * BK && n % 8 == 0 && wide && (int64_t)ldc * 2 * T::BM < (1ll << 31))) return false;
+  const int64_t tiles = tile_count(m, n, num_chunks, T::BM, T::BN);
+  const int64_t grid = tiles < device_cu_count() ? tiles : device_cu_count();
+  gemm_pingpong_bf16_kernel<T><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
+      a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
+  err = hipGetLastError();
+  return true;
+}
+
 template <int EPI>
 hipError_t launch_split(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs, int64_t m, int64_t n,
                         int64_t k, uint16_t* c, int64_t ldc, int num_chunks, int first_chunk, int* chunk_done,
@@ -1168,13 +1257,10 @@ hipError_t launch_split(const uint8_t* a, const uint8_t* as, const uint8_t* b, c
   const int64_t tiles = tile_count(m, n, num_chunks, T::BM, T::BN);
   const int64_t grid = tiles < device_cu_count() ? tiles : device_cu_count();
   const int wide = ((uintptr_t)c % 16 == 0 && ldc % 8 == 0) ? 1 : 0;
-  // BF16 output in whole 16-byte segments, at least two K steps, tile offsets in 32 bits: the
-  // two-group kernel, which also overlaps each epilogue with the next tile's first loads
-  if (EPI == EPI_BF16 && k >= 2 * BK && n % 8 == 0 && wide && (int64_t)ldc * 2 * T::BM < (1ll << 31)) {
-    gemm_pingpong_bf16_kernel<T><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
-        a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
-    return hipGetLastError();
-  }
+  hipError_t err = hipSuccess;
+  if (EPI == EPI_BF16 &&
+      launch_two_group<T>(a, as, b, bs, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream, err))
+    return err;
   gemm_kernel<T, 1, 1, EPI><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
       a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done, wide, sg);
   return hipGetLastError();
@@ -1230,8 +1316,13 @@ hipError_t launch_gemm(const uint8_t* a, const uint8_t* as, int a_layout, const 
       if (split_ring_fits(as, a_layout, bs, b_layout, m, num_chunks))
         return launch_split<EPI_BF16>(a, as, b, bs, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
       return launch_cfg<TileL>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
-    case CFG_N:
+    case CFG_N: {
+      hipError_t err = hipSuccess;
+      if (split_ring_fits(as, a_layout, bs, b_layout, m, num_chunks) &&
+          launch_two_group<TileNR>(a, as, b, bs, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream, err))
+        return err;
       return launch_cfg<TileN>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
+    }
     case CFG_Q:
       return launch_cfg<TileQ>(a, as, a_layout, b, bs, b_layout, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);
     case CFG_R:

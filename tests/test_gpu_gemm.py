@@ -332,6 +332,27 @@ def test_gemm_two_group_kernel_every_last_step(kt):
         _assert_close(c_two, ref, _abs_sum_full(qa, sa[1], 1, qb, sb[1], 1), f"two-group k={k}")
 
 
+@pytest.mark.parametrize("kt", [2, 3, 7, 13])
+def test_gemm_two_group_256x192(kt):
+    """256 x 192 tiles (the M = 2048-4096 workloads) with swizzled scales and 16-byte aligned
+    output rows run on the two-group kernel; with rows 8 bytes off that alignment on the staged
+    kernel. Ragged M and N tails (232 rows, 104 columns in the last tiles), each run after a
+    decoy product: the same bits, and the oracle's at one K."""
+    m, n, chunks, k = 1000, 12200, 1, 128 * kt
+    assert mx.gemm_tiles_per_chunk(m, n, chunks) == 4 * 64
+    print(f"two-group 256x192 k={k}", flush=True)
+    qa, sa, qb, sb = _operands(m, n, k, seed_a=kt + 50, seed_b=kt + 51)
+    xa, xsa, xb, xsb = _operands(m, n, k, seed_a=kt + 52, seed_b=kt + 53)
+    _gpu_gemm(xa, xsa[1], 1, xb, xsb[1], 1, pad_cols=8)
+    c_two = _gpu_gemm(qa, sa[1], 1, qb, sb[1], 1, pad_cols=8)
+    _gpu_gemm(xa, xsa[1], 1, xb, xsb[1], 1, pad_cols=4)
+    c_staged = _gpu_gemm(qa, sa[1], 1, qb, sb[1], 1, pad_cols=4)
+    assert np.array_equal(c_two, c_staged), f"k={k}"
+    if kt == 7:
+        ref = oracle.gemm(qa, sa[1], 1, qb, sb[1], 1)
+        _assert_close(c_two, ref, _abs_sum_full(qa, sa[1], 1, qb, sb[1], 1), f"two-group 256x192 k={k}")
+
+
 @pytest.mark.parametrize("m,n,k,chunks", [(64, 1, 128, 1), (33, 17, 256, 1), (200, 40, 16384, 2),
                                           (4, 300, 640, 4), (130, 3, 1152, 2)])
 def test_gemm_edge_shapes_full(m, n, k, chunks):
