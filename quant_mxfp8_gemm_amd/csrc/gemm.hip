@@ -691,7 +691,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
 //    are dropped), so every wave issues the same 16 stores, and the next tile's first waits let
 //    exactly those stay in flight. 256 x 192 (two tiles per compute unit at most, for the
 //    M = 2048-4096 workloads): the whole tile is staged once the loads have landed.
-template <class T>
+template <class T, bool CHAIN>
 __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, uint16_t* __restrict__ C, int M, int N, int K, int ldc, int num_chunks,
@@ -809,19 +809,20 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     const int so = live ? kt * (int)scale_step<1>() : 0;
     sc.a = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(make_rsrc(As, live ? sa_bytes : 0u), ts.sa_off, so, 0));
   };
-  auto load_sb = [&](const TileState& ts, int kt, Scales& sc) {
+  auto load_sb_at = [&](const uint32_t (&sb_off)[NSB], int kt, Scales& sc) {
     const bool live = kt < KT;
     const int so = live ? kt * (int)scale_step<1>() : 0;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(Bs, live ? sb_bytes : 0u);
     if constexpr (NSB == 1) {
-      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ts.sb_off[0], so, 0));
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, sb_off[0], so, 0));
 #pragma unroll
       for (int t = 0; t < TN; ++t) sc.b[t] = v[t];
     } else {
 #pragma unroll
-      for (int t = 0; t < TN; ++t) sc.b[t] = __builtin_amdgcn_raw_buffer_load_b32(r, ts.sb_off[t], so, 0);
+      for (int t = 0; t < TN; ++t) sc.b[t] = __builtin_amdgcn_raw_buffer_load_b32(r, sb_off[t], so, 0);
     }
   };
+  auto load_sb = [&](const TileState& ts, int kt, Scales& sc) { load_sb_at(ts.sb_off, kt, sc); };
   // a tile's first loads, in the loop's order (B(s + 1) and the B scales issued last before
   // step s), so that the counts and the compiler's own waits for the scales see the same loads
   // in flight
@@ -846,8 +847,16 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
 
   int bid = blockIdx.x;
   if (bid >= total) return;
-  TileState cur;
+  // With a multiple of six K steps (and the overlapped epilogue) the ring slots of a tile's
+  // first steps are those its predecessor's last steps would fill next: the last two steps
+  // then issue the next tile's first loads in place of the dropped ones, and the epilogue
+  // issues none (eight waves issuing them at once there kept the address path busy for
+  // thousands of cycles).
+  static_assert(!CHAIN || OVL, "chained tiles need the overlapped epilogue");
+  // chained: the next tile's state is set up a tile ahead (where the matrix pipes idle anyway)
+  TileState cur, nxt;
   setup(bid, cur);
+  if constexpr (CHAIN) setup(bid + (int)gridDim.x < total ? bid + (int)gridDim.x : bid, nxt);
   Scales sc2[2];
   first_loads(cur, sc2[0]);
   if constexpr (OVL) {
@@ -862,6 +871,8 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
   }
 
   while (true) {
+    const bool has_next = bid + (int)gridDim.x < total;
+    const int done_m0 = cur.m0, done_m_end = cur.m_end, done_n0 = cur.n0, done_chunk = cur.chunk;
     // per-lane LDS bases of the fragment reads: A slot 0 (slot 1 at +32 KiB), B slot 0 (slots
     // 1 and 2 at + B_BYTES and + 2 B_BYTES, or slot 2 from a base of its own when it lies beyond
     // the reach of an instruction offset); the block offsets t * 4 KiB and the slot offsets are
@@ -936,17 +947,27 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     // (into the slot of step s - 1, which both groups have finished reading) and the B scales of
     // step s + 1. In a tile's first step the previous tile's C stores may still be in flight
     // behind B(1) and the B scales of step 0.
-    auto stage = [&](auto Jc, int s, auto First) {
+    // Mode: 0 any step, 1 the second-to-last step of a chained tile (B(s + 2) is the next tile's
+    // B(0)), 2 its last step (every load is the next tile's, and nothing is waited for: this
+    // tile's data has landed)
+    auto stage = [&](auto Jc, int s, auto First, auto Mode) {
       constexpr int J = decltype(Jc)::value;
       constexpr bool FIRST = decltype(First)::value;
+      constexpr int MODE = decltype(Mode)::value;
       constexpr int AS = J & 1, BS = J % 3, CUR = J & 1, NXT = (J + 1) & 1;
       v8i af[T::TM], bf[TN];
       // memory, first half
       read_frags(AS, BS, 0, af, bf);
       __builtin_amdgcn_sched_barrier(0);
-      load_sa(cur, s + 1, sc2[NXT]);
-      __builtin_amdgcn_sched_barrier(0);
-      issue_a(cur, s + 1, AS ^ 1);
+      if constexpr (MODE == 2) {
+        load_sa(nxt, has_next ? 0 : KT, sc2[NXT]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_a(nxt, has_next ? 0 : KT, AS ^ 1);
+      } else {
+        load_sa(cur, s + 1, sc2[NXT]);
+        __builtin_amdgcn_sched_barrier(0);
+        issue_a(cur, s + 1, AS ^ 1);
+      }
       phase_end();
       // compute, first half
       __builtin_amdgcn_s_setprio(1);
@@ -958,14 +979,22 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
       // which the first group reads it
       read_frags(AS, BS, 1, af, bf);
       __builtin_amdgcn_sched_barrier(0);
-      issue_b(cur, s + 2, (J + 2) % 3);
-      __builtin_amdgcn_sched_barrier(0);
-      load_sb(cur, s + 1, sc2[NXT]);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (FIRST)
-        wait_vm<C_STORES + 2 * NSB + 1 + T::DA + T::DB>();
+      if constexpr (MODE == 0)
+        issue_b(cur, s + 2, (J + 2) % 3);
       else
+        issue_b(nxt, has_next ? MODE - 1 : KT, (J + 2) % 3);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (MODE == 2)
+        load_sb(nxt, has_next ? 0 : KT, sc2[NXT]);
+      else
+        load_sb(cur, s + 1, sc2[NXT]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (MODE == 2) {
+      } else if constexpr (FIRST) {
+        wait_vm<C_STORES + 2 * NSB + 1 + T::DA + T::DB>();
+      } else {
         wait_vm<2 * NSB + 1 + T::DA + T::DB>();
+      }
       phase_end();
       // compute, second half; then A(s + 1) has landed (behind it: B(s + 2) and the B scales of
       // s + 1), before the barrier after which this group reads it
@@ -973,7 +1002,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
       mma_half(1, af, bf, sc2[CUR]);
       __builtin_amdgcn_s_setprio(0);
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm<T::DB + NSB>();
+      if constexpr (MODE != 2) wait_vm<T::DB + NSB>();
       phase_end();
     };
 
@@ -987,25 +1016,55 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     // then six steps per iteration, left after the last step wherever it falls (a wait count
     // chosen at run time inside a step would split it, and the compiler then spills)
     using No = std::integral_constant<bool, false>;
-    stage(std::integral_constant<int, 0>{}, 0, std::integral_constant<bool, true>{});
-    if (KT > 1) {
+    using M0 = std::integral_constant<int, 0>;
+    stage(std::integral_constant<int, 0>{}, 0, std::integral_constant<bool, true>{}, M0{});
+    if constexpr (CHAIN) {
+      // K steps a multiple of six: whole groups of six, then the last five steps straight
+      // (the last two issuing the next tile's first loads)
+      for (int s = 1; s + 11 <= KT; s += 6) {
+        stage(std::integral_constant<int, 1>{}, s, No{}, M0{});
+        stage(std::integral_constant<int, 2>{}, s + 1, No{}, M0{});
+        stage(std::integral_constant<int, 3>{}, s + 2, No{}, M0{});
+        stage(std::integral_constant<int, 4>{}, s + 3, No{}, M0{});
+        stage(std::integral_constant<int, 5>{}, s + 4, No{}, M0{});
+        stage(std::integral_constant<int, 0>{}, s + 5, No{}, M0{});
+      }
+      // (exits the compiler cannot rule out split the five steps into blocks as in the loop;
+      // as one block their fragment registers were spilled)
+      int kt_o = KT;
+      asm volatile("" : "+s"(kt_o));
+      do {
+        stage(std::integral_constant<int, 1>{}, KT - 5, No{}, M0{});
+        if (kt_o < 0) break;
+        stage(std::integral_constant<int, 2>{}, KT - 4, No{}, M0{});
+        if (kt_o < 0) break;
+        stage(std::integral_constant<int, 3>{}, KT - 3, No{}, M0{});
+        if (kt_o < 0) break;
+        stage(std::integral_constant<int, 4>{}, KT - 2, No{}, std::integral_constant<int, 1>{});
+        if (kt_o < 0) break;
+        stage(std::integral_constant<int, 5>{}, KT - 1, No{}, std::integral_constant<int, 2>{});
+      } while (false);
+    } else if (KT > 1) {
       for (int s = 1;; s += 6) {
-        stage(std::integral_constant<int, 1>{}, s, No{});
+        stage(std::integral_constant<int, 1>{}, s, No{}, M0{});
         if (s + 1 >= KT) break;
-        stage(std::integral_constant<int, 2>{}, s + 1, No{});
+        stage(std::integral_constant<int, 2>{}, s + 1, No{}, M0{});
         if (s + 2 >= KT) break;
-        stage(std::integral_constant<int, 3>{}, s + 2, No{});
+        stage(std::integral_constant<int, 3>{}, s + 2, No{}, M0{});
         if (s + 3 >= KT) break;
-        stage(std::integral_constant<int, 4>{}, s + 3, No{});
+        stage(std::integral_constant<int, 4>{}, s + 3, No{}, M0{});
         if (s + 4 >= KT) break;
-        stage(std::integral_constant<int, 5>{}, s + 4, No{});
+        stage(std::integral_constant<int, 5>{}, s + 4, No{}, M0{});
         if (s + 5 >= KT) break;
-        stage(std::integral_constant<int, 0>{}, s + 5, No{});
+        stage(std::integral_constant<int, 0>{}, s + 5, No{}, M0{});
         if (s + 6 >= KT) break;
       }
     }
     if (!grp) phase_end();  // the first group meets the second group's last barrier
-    wait_vm<0>();           // the dropped loads too: nothing writes LDS under the epilogue
+    // every load of this tile has landed (the last ones were waited for a step ago when
+    // chained); unchained, wait for the dropped ones too: nothing may write LDS under the
+    // epilogue (chained, the next tile's loads write A slot 0 and B slots 0 and 1 only)
+    if constexpr (!CHAIN) wait_vm<0>();
     // the scale registers stay live past the loop: otherwise the compiler sinks each step's scale
     // loads into the next step (their only use, behind an early exit), right before the MFMAs
     asm volatile("" ::"v"(sc2[0].a), "v"(sc2[1].a));
@@ -1016,9 +1075,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     int tid_e = tid;
     asm volatile("" : "+v"(tid_e));
     const int e32 = tid_e & 31, eg = (tid_e >> 5) & 1;
-    const TileState done = cur;
     const int nbid = bid + (int)gridDim.x;
-    const bool has_next = nbid < total;
     if constexpr (OVL) {
       // ---- epilogue, with the next tile's first loads issued half-way.
       // Quarter qd = (y, h): tile rows 64 wm + 32 y + [0, 32) of every wm and tile columns
@@ -1045,14 +1102,19 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
       // loads are issued, so that its offsets and this tile's remaining accumulators fit
       stage_quarter(0, stage0);
       stage_quarter(1, stage1);
-      if (has_next) {
+      if constexpr (CHAIN) {
+        // the next tile's loads are in flight; set up the one after it
+        cur = nxt;
+        const int nnbid = nbid + (int)gridDim.x;
+        setup(nnbid < total ? nnbid : nbid, nxt);
+      } else if (has_next) {
         setup(nbid, cur);
         first_loads(cur, sc2[0]);
       }
       // C through a resource over this tile's rows: elements past the last row or column get
       // an offset past its end and are dropped, so every wave issues the same 16 stores
-      const uint32_t c_bytes = (uint32_t)(done.m_end - done.m0) * (uint32_t)ldc * 2u;
-      const __amdgpu_buffer_rsrc_t rc = make_rsrc(C + (int64_t)done.m0 * ldc, c_bytes);
+      const uint32_t c_bytes = (uint32_t)(done_m_end - done_m0) * (uint32_t)ldc * 2u;
+      const __amdgpu_buffer_rsrc_t rc = make_rsrc(C + (int64_t)done_m0 * ldc, c_bytes);
       auto store_quarter = [&](int qd, const uint8_t* st) {
         const int y = qd >> 1, h = qd & 1;
 #pragma unroll
@@ -1061,8 +1123,8 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
           const int rq = p >> 4, chunk = p & 15;
           const u32x4 v = *(const u32x4*)(st + rq * 256 + ((chunk ^ (rq & 7)) * 16));
           const int r = (rq >> 5) * 64 + y * 32 + (rq & 31);  // tile row
-          const int n = done.n0 + (chunk >> 3) * 128 + h * 64 + (chunk & 7) * 8;
-          const bool ok = done.m0 + r < done.m_end && n < N;
+          const int n = done_n0 + (chunk >> 3) * 128 + h * 64 + (chunk & 7) * 8;
+          const bool ok = done_m0 + r < done_m_end && n < N;
           const uint32_t off = ok ? ((uint32_t)r * (uint32_t)ldc + (uint32_t)n) * 2u : 0x80000000u;
           __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 2);
         }
@@ -1101,9 +1163,9 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
       for (int p = tid_e; p < BM * SEGS; p += T::NT) {
         const int r = p / SEGS;
         const int c8 = (p % SEGS) * 8;
-        const int m = done.m0 + r;
-        const int n = done.n0 + c8;
-        if (m >= done.m_end || n >= N) continue;
+        const int m = done_m0 + r;
+        const int n = done_n0 + c8;
+        if (m >= done_m_end || n >= N) continue;
         uint4 v = *(const uint4*)(smem + r * T::C_STRIDE + c8 * 2);
         if (((r >> 3) ^ (r >> 4)) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
         __builtin_nontemporal_store(*(const u32x4*)&v, (u32x4*)(C + (int64_t)m * ldc + n));
@@ -1118,11 +1180,14 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     if (chunk_done != nullptr) {
       __threadfence();  // this thread's C stores are visible device-wide
       __syncthreads();
-      if (tid == 0) atomicAdd(chunk_done + done.chunk, 1);
+      if (tid == 0) atomicAdd(chunk_done + done_chunk, 1);
     }
     if (!has_next) break;
     bid = nbid;
   }
+  // (chained, the last tile's last steps issued dropped loads that write no LDS this workgroup
+  // reads; they complete before its waves end)
+  wait_vm<0>();
 #endif
 }
 
@@ -1243,8 +1308,13 @@ bool launch_two_group(const uint8_t* a, const uint8_t* as, const uint8_t* b, con
   if (!(k >= 2 * BK && n % 8 == 0 && wide && (int64_t)ldc * 2 * T::BM < (1ll << 31))) return false;
   const int64_t tiles = tile_count(m, n, num_chunks, T::BM, T::BN);
   const int64_t grid = tiles < device_cu_count() ? tiles : device_cu_count();
-  gemm_pingpong_bf16_kernel<T><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
-      a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
+  // with the overlapped epilogue and a multiple of six K steps, consecutive tiles chain their loads
+  if (T::BN == 256 && k % (6 * BK) == 0)
+    gemm_pingpong_bf16_kernel<T, T::BN == 256><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
+        a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
+  else
+    gemm_pingpong_bf16_kernel<T, false><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
+        a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
   err = hipGetLastError();
   return true;
 }
