@@ -691,7 +691,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
 //    are dropped), so every wave issues the same 16 stores, and the next tile's first waits let
 //    exactly those stay in flight. 256 x 192 (two tiles per compute unit at most, for the
 //    M = 2048-4096 workloads): the whole tile is staged once the loads have landed.
-template <class T, bool CHAIN>
+template <class T, int CH>
 __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, uint16_t* __restrict__ C, int M, int N, int K, int ldc, int num_chunks,
@@ -852,7 +852,10 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
   // then issue the next tile's first loads in place of the dropped ones, and the epilogue
   // issues none (eight waves issuing them at once there kept the address path busy for
   // thousands of cycles).
-  static_assert(!CHAIN || OVL, "chained tiles need the overlapped epilogue");
+  // CH: 0, or for chained tiles (K steps even, KT - 1 = CH mod 6) the number of steps after the
+  // last whole group of six
+  static_assert(CH == 0 || (OVL && (CH == 1 || CH == 3 || CH == 5)), "chained tiles: even K steps, overlapped epilogue");
+  constexpr bool CHAIN = CH != 0;
   // chained: the next tile's state is set up a tile ahead (where the matrix pipes idle anyway)
   TileState cur, nxt;
   setup(bid, cur);
@@ -979,10 +982,13 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
       // which the first group reads it
       read_frags(AS, BS, 1, af, bf);
       __builtin_amdgcn_sched_barrier(0);
+      // B(s + 2) goes to slot (J + 2) mod 3; past this tile, the next tile's B(0) and B(1) go to
+      // slots 0 and 1, so a chained step fills those with them (slot 2 is left alone)
+      constexpr int BT = (J + 2) % 3;
       if constexpr (MODE == 0)
-        issue_b(cur, s + 2, (J + 2) % 3);
-      else
-        issue_b(nxt, has_next ? MODE - 1 : KT, (J + 2) % 3);
+        issue_b(cur, s + 2, BT);
+      else if constexpr (BT < 2)
+        issue_b(nxt, has_next ? BT : KT, BT);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (MODE == 2)
         load_sb(nxt, has_next ? 0 : KT, sc2[NXT]);
@@ -1008,8 +1014,8 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
 
     // B(0), the A scales of step 0 and A(0) have landed; B(1), the B scales of step 0 and the C
     // stores issued after them (the previous tile's, or before the first tile dropped ones) may
-    // still be in flight
-    wait_vm<T::DB + NSB + C_STORES>();
+    // still be in flight (chained with CH = 3, B(0) was issued last, right before the stores)
+    wait_vm<(CH == 3 ? 0 : T::DB + NSB) + C_STORES>();
     phase_end();
     if (grp) phase_end();  // the second group starts one phase late
     // The first step on its own (its count lets the previous tile's C stores stay in flight),
@@ -1019,9 +1025,9 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     using M0 = std::integral_constant<int, 0>;
     stage(std::integral_constant<int, 0>{}, 0, std::integral_constant<bool, true>{}, M0{});
     if constexpr (CHAIN) {
-      // K steps a multiple of six: whole groups of six, then the last five steps straight
-      // (the last two issuing the next tile's first loads)
-      for (int s = 1; s + 11 <= KT; s += 6) {
+      // whole groups of six, then the last CH steps straight (the last two issuing the next
+      // tile's first loads)
+      for (int s = 1; s + 6 + CH <= KT; s += 6) {
         stage(std::integral_constant<int, 1>{}, s, No{}, M0{});
         stage(std::integral_constant<int, 2>{}, s + 1, No{}, M0{});
         stage(std::integral_constant<int, 3>{}, s + 2, No{}, M0{});
@@ -1029,20 +1035,25 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
         stage(std::integral_constant<int, 5>{}, s + 4, No{}, M0{});
         stage(std::integral_constant<int, 0>{}, s + 5, No{}, M0{});
       }
-      // (exits the compiler cannot rule out split the five steps into blocks as in the loop;
+      // (exits the compiler cannot rule out split the last steps into blocks as in the loop;
       // as one block their fragment registers were spilled)
       int kt_o = KT;
       asm volatile("" : "+s"(kt_o));
+      auto tail = [&](auto Jc) {
+        constexpr int J = decltype(Jc)::value;
+        if constexpr (J <= CH)
+          stage(Jc, KT - CH - 1 + J, No{}, std::integral_constant<int, J == CH ? 2 : J == CH - 1 ? 1 : 0>{});
+      };
       do {
-        stage(std::integral_constant<int, 1>{}, KT - 5, No{}, M0{});
+        tail(std::integral_constant<int, 1>{});
+        if (CH == 1 || kt_o < 0) break;
+        tail(std::integral_constant<int, 2>{});
         if (kt_o < 0) break;
-        stage(std::integral_constant<int, 2>{}, KT - 4, No{}, M0{});
+        tail(std::integral_constant<int, 3>{});
+        if (CH == 3 || kt_o < 0) break;
+        tail(std::integral_constant<int, 4>{});
         if (kt_o < 0) break;
-        stage(std::integral_constant<int, 3>{}, KT - 3, No{}, M0{});
-        if (kt_o < 0) break;
-        stage(std::integral_constant<int, 4>{}, KT - 2, No{}, std::integral_constant<int, 1>{});
-        if (kt_o < 0) break;
-        stage(std::integral_constant<int, 5>{}, KT - 1, No{}, std::integral_constant<int, 2>{});
+        tail(std::integral_constant<int, 5>{});
       } while (false);
     } else if (KT > 1) {
       for (int s = 1;; s += 6) {
@@ -1061,10 +1072,16 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
       }
     }
     if (!grp) phase_end();  // the first group meets the second group's last barrier
-    // every load of this tile has landed (the last ones were waited for a step ago when
-    // chained); unchained, wait for the dropped ones too: nothing may write LDS under the
-    // epilogue (chained, the next tile's loads write A slot 0 and B slots 0 and 1 only)
-    if constexpr (!CHAIN) wait_vm<0>();
+    // Every load of this tile has landed (chained, the last ones were waited for a step ago).
+    // Nothing may write the epilogue's staging slots (A slot 1, B slot 2) under it: unchained,
+    // wait for the dropped loads too; chained, the next tile's loads write A slot 0 and B slots
+    // 0 and 1 only, but with one step after the last group (CH = 1) the step before it dropped
+    // a B load into slot 2 (11 loads behind it: its B scales, the next tile's A scales, A(0),
+    // B(0) and B scales)
+    if constexpr (!CHAIN)
+      wait_vm<0>();
+    else if constexpr (CH == 1)
+      wait_vm<3 * NSB + T::DA + T::DB - 1>();
     // the scale registers stay live past the loop: otherwise the compiler sinks each step's scale
     // loads into the next step (their only use, behind an early exit), right before the MFMAs
     asm volatile("" ::"v"(sc2[0].a), "v"(sc2[1].a));
@@ -1103,8 +1120,11 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
       stage_quarter(0, stage0);
       stage_quarter(1, stage1);
       if constexpr (CHAIN) {
-        // the next tile's loads are in flight; set up the one after it
+        // the next tile's loads are in flight but for B(0) (CH = 3) or B(1) (CH = 1), whose slot
+        // the last step was reading; set up the tile after it
         cur = nxt;
+        if constexpr (CH == 3) issue_b(cur, has_next ? 0 : KT, 0);
+        if constexpr (CH == 1) issue_b(cur, has_next ? 1 : KT, 1);
         const int nnbid = nbid + (int)gridDim.x;
         setup(nnbid < total ? nnbid : nbid, nxt);
       } else if (has_next) {
@@ -1308,12 +1328,21 @@ bool launch_two_group(const uint8_t* a, const uint8_t* as, const uint8_t* b, con
   if (!(k >= 2 * BK && n % 8 == 0 && wide && (int64_t)ldc * 2 * T::BM < (1ll << 31))) return false;
   const int64_t tiles = tile_count(m, n, num_chunks, T::BM, T::BN);
   const int64_t grid = tiles < device_cu_count() ? tiles : device_cu_count();
-  // with the overlapped epilogue and a multiple of six K steps, consecutive tiles chain their loads
-  if (T::BN == 256 && k % (6 * BK) == 0)
-    gemm_pingpong_bf16_kernel<T, T::BN == 256><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
+  // with the overlapped epilogue and an even number of K steps, consecutive tiles chain their
+  // loads; the variant follows the number of steps after the last whole group of six
+  const int kt = (int)(k / BK);
+  constexpr int CH5 = T::BN == 256 ? 5 : 0, CH3 = T::BN == 256 ? 3 : 0, CH1 = T::BN == 256 ? 1 : 0;
+  if (T::BN == 256 && kt % 6 == 0)
+    gemm_pingpong_bf16_kernel<T, CH5><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
+        a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
+  else if (T::BN == 256 && kt % 6 == 4)
+    gemm_pingpong_bf16_kernel<T, CH3><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
+        a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
+  else if (T::BN == 256 && kt % 6 == 2)
+    gemm_pingpong_bf16_kernel<T, CH1><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
         a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
   else
-    gemm_pingpong_bf16_kernel<T, false><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
+    gemm_pingpong_bf16_kernel<T, 0><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
         a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
   err = hipGetLastError();
   return true;
