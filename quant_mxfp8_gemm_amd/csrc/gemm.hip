@@ -111,6 +111,15 @@ __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 // refilled or reread under a pending access; the epilogue's global stores need not drain.
 __device__ __forceinline__ void block_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// An 8-byte LDS store that the compiler does not see as one. The compiler cannot tell which LDS
+// bytes an LDS-DMA load in flight writes, so it makes a store to LDS wait for all of them; this
+// store is for LDS that the caller knows no load in flight targets. It completes in order with
+// the wave's other LDS accesses (a later wait on lgkmcnt covers it).
+__device__ __forceinline__ void lds_store_b64_unordered(uint8_t* p, u32x2 v) {
+  const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)p;
+  asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+
 // Wait until at most N of this wave's vector memory operations are outstanding. They
 // complete in issue order, so this means every load issued before the last N has landed.
 template <int N>
@@ -1083,10 +1092,17 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     else if constexpr (CH == 1)
       wait_vm<3 * NSB + T::DA + T::DB - 1>();
     // the scale registers stay live past the loop: otherwise the compiler sinks each step's scale
-    // loads into the next step (their only use, behind an early exit), right before the MFMAs
-    asm volatile("" ::"v"(sc2[0].a), "v"(sc2[1].a));
+    // loads into the next step (their only use, behind an early exit), right before the MFMAs.
+    // Chained, set 0 holds the next tile's first scales, still in flight: a use here would wait
+    // for them and for every first load issued before them
+    if constexpr (!CHAIN) {
+      asm volatile("" ::"v"(sc2[0].a));
 #pragma unroll
-    for (int t = 0; t < TN; ++t) asm volatile("" ::"v"(sc2[0].b[t]), "v"(sc2[1].b[t]));
+      for (int t = 0; t < TN; ++t) asm volatile("" ::"v"(sc2[0].b[t]));
+    }
+    asm volatile("" ::"v"(sc2[1].a));
+#pragma unroll
+    for (int t = 0; t < TN; ++t) asm volatile("" ::"v"(sc2[1].b[t]));
 
     block_barrier();  // every wave's loads have landed and its reads are done
     int tid_e = tid;
@@ -1111,7 +1127,8 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
             const int chunk = wn * 8 + xx * 4 + q;
             const uint32_t lo = pack_bf16x2(acc[x][y][4 * q + 0], acc[x][y][4 * q + 1]);
             const uint32_t hi = pack_bf16x2(acc[x][y][4 * q + 2], acc[x][y][4 * q + 3]);
-            *(uint2*)(st + rq * 256 + ((chunk ^ (rq & 7)) * 16) + eg * 8) = make_uint2(lo, hi);
+            // the next tile's loads in flight write A slot 0 and B slots 0 and 1 only
+            lds_store_b64_unordered(st + rq * 256 + ((chunk ^ (rq & 7)) * 16) + eg * 8, u32x2{lo, hi});
           }
         }
       };
