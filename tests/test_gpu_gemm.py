@@ -353,6 +353,24 @@ def test_gemm_two_group_256x192(kt):
         _assert_close(c_two, ref, _abs_sum_full(qa, sa[1], 1, qb, sb[1], 1), f"two-group 256x192 k={k}")
 
 
+@pytest.mark.parametrize("kt", [2, 4, 6, 8, 10, 12])
+def test_gemm_two_group_256x192_two_tiles(kt):
+    """Two 256 x 192 tiles per workgroup on the two-group kernel (512 tiles in two chunks of
+    1000 rows, ragged in M and N; the second tile's first loads issued in the first tile's
+    epilogue): the same bits as the staged kernel (rows 8 bytes off alignment), each run after a
+    decoy product."""
+    m, n, chunks, k = 2000, 12200, 2, 128 * kt
+    assert mx.gemm_tiles_per_chunk(m, n, chunks) == 4 * 64
+    print(f"two-group 256x192 two tiles k={k}", flush=True)
+    qa, sa, qb, sb = _operands(m, n, k, seed_a=kt + 60, seed_b=kt + 61)
+    xa, xsa, xb, xsb = _operands(m, n, k, seed_a=kt + 62, seed_b=kt + 63)
+    _gpu_gemm(xa, xsa[1], 1, xb, xsb[1], 1, pad_cols=8, num_chunks=chunks)
+    c_two = _gpu_gemm(qa, sa[1], 1, qb, sb[1], 1, pad_cols=8, num_chunks=chunks)
+    _gpu_gemm(xa, xsa[1], 1, xb, xsb[1], 1, pad_cols=4, num_chunks=chunks)
+    c_staged = _gpu_gemm(qa, sa[1], 1, qb, sb[1], 1, pad_cols=4, num_chunks=chunks)
+    assert np.array_equal(c_two, c_staged), f"k={k}"
+
+
 @pytest.mark.parametrize("m,n,k,chunks", [(64, 1, 128, 1), (33, 17, 256, 1), (200, 40, 16384, 2),
                                           (4, 300, 640, 4), (130, 3, 1152, 2)])
 def test_gemm_edge_shapes_full(m, n, k, chunks):
