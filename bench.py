@@ -55,8 +55,8 @@ def _parse():
 # counter of a 1 GiB copy onto 1 GiB. Valid only for the kernel code it was taken on
 # (gemm_code_sha256).
 GEMM_TRAFFIC = {
-    "source_sha256": "b6a2b7fd253d51e8e43900dd85c10f00b877c99271f2c32a0ffab4c0f597e31d",
-    "fetch_kib": 456385.0, "write_kib": 393301.5,
+    "source_sha256": "a0d3950d521ca0b0bd6b3a2d5d63476df38fbb18ea9c03b4f53b25a80b6a9fc9",
+    "fetch_kib": 456460.8, "write_kib": 393302.7,
     "fetch_factor": 2.0, "write_factor": 1.0,
 }
 
