@@ -22,10 +22,10 @@
 //    stage buffers and B in three (B fetched two steps ahead, all 160 KiB of LDS), the scales
 //    of a wave's rows loaded one step ahead into registers with one 8-byte and one 16-byte
 //    load (rows r, r+32, r+64, r+96 of a swizzled 128-row group are adjacent). With BF16
-//    output in whole 16-byte segments it runs as two wave groups that take turns on each
-//    SIMD's matrix pipe (one issues a half step's MFMAs from registers while the other reads
-//    its next fragments from LDS and issues the loads), with a barrier between turns
-//    (gemm_pingpong_bf16_kernel). Otherwise (the fused gate_up epilogue, unaligned output)
+//    output in whole 16-byte segments it, and the 256 x 192 tile, run as two wave groups that
+//    take turns on each SIMD's matrix pipe (one issues a half step's MFMAs from registers while
+//    the other reads its next fragments from LDS and issues the loads), with a barrier between
+//    turns (gemm_pingpong_bf16_kernel). Otherwise (the fused gate_up epilogue, unaligned output)
 //    its A refill (and the refills of the staged tiles of up to 128 rows) is issued between
 //    the two 64-K halves of a step and its B refill after the step's MFMAs, so the step's
 //    first fragment reads and MFMAs follow the barrier at once. With at most 32 rows in one chunk (decode)
@@ -49,7 +49,8 @@
 //    stage are one aligned dword in both scale layouts.
 //  * Epilogue: the tile is converted to BF16 into LDS (over the stage buffers, rows padded by
 //    16 bytes) and written back with 16-byte streaming stores, every row a run of full lines.
-//    The two-group BF16 kernel instead issues the next tile's first loads before writing the
+//    The two-group BF16 kernel on 256 x 256 tiles instead has the next tile's first loads in
+//    flight (issued by the last K steps when the number of K steps is even) while it writes the
 //    tile out in four 32 KiB quarters through the two ring slots those loads leave free, and
 //    lets the stores drain under the next tile's first step: all 256 workgroups finish their
 //    tiles together, and their stores alone exceed what HBM takes in that time.
