@@ -718,9 +718,13 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
   static_assert(A_RING + 2 * T::A_BYTES <= 160 * 1024, "ring");
   // B slot 2 lies beyond the 64 KiB reach of an instruction offset from the slot-0 base
   constexpr bool FAR_B2 = 2 * T::B_BYTES + (TN - 1) * 32 * 128 + 32 * 128 > 65536;
-  // B scale loads per step: one 16-byte load of the wave's four row blocks (256 x 256, where
-  // they are one swizzled 128-row group), else one per row block
-  constexpr int NSB = BN == 256 ? 1 : TN;
+  // B scale loads per step: one 16-byte load. 256 x 256: the wave's four row blocks, one
+  // swizzled 128-row group. 256 x 192: the wave's three blocks start at block q of a group and
+  // may run into the next one, so lanes 0-31 load the group of the first block and lanes 32-63
+  // the group after it, and a lane-half swap gives every lane both (SB_TWO_GROUPS)
+  constexpr int NSB = 1;
+  constexpr bool SB_TWO_GROUPS = BN == 192;
+  constexpr int SBW = SB_TWO_GROUPS ? 4 : TN;  // B scale dwords a lane keeps per step
   constexpr int C_STORES = OVL ? 16 : 0;  // C stores per thread and tile left in flight
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::LDS_BYTES];
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -750,6 +754,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
   struct TileState {
     int m0, m_end, n0, chunk;
     uint32_t a_off[T::DA], b_off[T::DB], sa_off, sb_off[NSB];
+    int sbq;  // 256 x 192: the swizzled 32-row block (0-3) of the wave's first B row block
   };
   auto setup = [&](int bid, TileState& ts) {
     const int ci = bid / tpc;
@@ -785,12 +790,16 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     }
     // rows r, r + 32, r + 64, r + 96 of a swizzled 128-row group keep their 4-byte scale groups
     // side by side: one 8-byte load for the wave's two A row blocks, one 16-byte load for the
-    // four B row blocks of a 128-column wave, one 4-byte load per block otherwise (rows past the
-    // operand read zero padding or 0; not stored)
+    // four B row blocks of a 128-column wave or, per lane half, for one of the two groups that
+    // the three blocks of a 96-column wave touch (rows past the operand read zero padding or 0;
+    // not stored)
     ts.sa_off = scale_base<1>((uint32_t)(ts.m0 + wm * T::WTM + (ln & 31)), nblk4);
-#pragma unroll
-    for (int t = 0; t < NSB; ++t)
-      ts.sb_off[t] = scale_base<1>((uint32_t)(ts.n0 + wn * T::WTN + 32 * t + (ln & 31)), nblk4);
+    const uint32_t c0 = (uint32_t)(ts.n0 + wn * T::WTN);  // a multiple of 32
+    ts.sbq = (int)(c0 >> 5) & 3;
+    if constexpr (SB_TWO_GROUPS)  // past the last group the load reads 0 (resource bound)
+      ts.sb_off[0] = scale_base<1>(((c0 >> 7) + (uint32_t)(ln >> 5)) * 128 + (uint32_t)(ln & 31), nblk4);
+    else
+      ts.sb_off[0] = scale_base<1>(c0 + (uint32_t)(ln & 31), nblk4);
   };
   // loads past the last step go through empty resources: dropped, but counted like the others
   auto issue_a = [&](const TileState& ts, int kt, int slot) {
@@ -812,7 +821,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
   // scale registers of one step: the wave's A row blocks, then its B row blocks
   struct Scales {
     u32x2 a;
-    uint32_t b[TN];
+    uint32_t b[SBW];
   };
   auto load_sa = [&](const TileState& ts, int kt, Scales& sc) {
     const bool live = kt < KT;
@@ -823,14 +832,9 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     const bool live = kt < KT;
     const int so = live ? kt * (int)scale_step<1>() : 0;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(Bs, live ? sb_bytes : 0u);
-    if constexpr (NSB == 1) {
-      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, sb_off[0], so, 0));
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, sb_off[0], so, 0));
 #pragma unroll
-      for (int t = 0; t < TN; ++t) sc.b[t] = v[t];
-    } else {
-#pragma unroll
-      for (int t = 0; t < TN; ++t) sc.b[t] = __builtin_amdgcn_raw_buffer_load_b32(r, sb_off[t], so, 0);
-    }
+    for (int t = 0; t < SBW; ++t) sc.b[t] = v[t];
   };
   auto load_sb = [&](const TileState& ts, int kt, Scales& sc) { load_sb_at(ts.sb_off, kt, sc); };
   // a tile's first loads, in the loop's order (B(s + 1) and the B scales issued last before
@@ -942,8 +946,28 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
       uint32_t as_sel[T::TM], bs_sel[TN];
 #pragma unroll
       for (int t = 0; t < T::TM; ++t) as_sel[t] = sc.a[t] >> (8 * g);
+      if constexpr (SB_TWO_GROUPS) {
+        // every lane gets both groups' dwords of its row (lanes 0-31 loaded the first group,
+        // d0-d3, lanes 32-63 the second, e0-e3), then block t's dword is number q + t of
+        // d0-d3 e0 e1, chosen by selects on the two bits of q (kept as registers: an indexed
+        // form would go through scratch memory)
+        const auto s0 = __builtin_amdgcn_permlane32_swap(sc.b[0], sc.b[0], false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(sc.b[1], sc.b[1], false, false);
+        const auto s2 = __builtin_amdgcn_permlane32_swap(sc.b[2], sc.b[2], false, false);
+        const auto s3 = __builtin_amdgcn_permlane32_swap(sc.b[3], sc.b[3], false, false);
+        uint32_t d0 = s0[0], d1 = s1[0], d2 = s2[0], d3 = s3[0], e0 = s0[1], e1 = s1[1];
+        asm volatile("" : "+v"(d0), "+v"(d1), "+v"(d2), "+v"(d3), "+v"(e0), "+v"(e1));
+        const bool q0 = cur.sbq & 1, q1 = cur.sbq & 2;
+        const uint32_t b0 = q1 ? (q0 ? d3 : d2) : (q0 ? d1 : d0);
+        const uint32_t b1 = q1 ? (q0 ? e0 : d3) : (q0 ? d2 : d1);
+        const uint32_t b2 = q1 ? (q0 ? e1 : e0) : (q0 ? d3 : d2);
+        bs_sel[0] = b0 >> (8 * g);
+        bs_sel[1] = b1 >> (8 * g);
+        bs_sel[2 % TN] = b2 >> (8 * g);
+      } else {
 #pragma unroll
-      for (int t = 0; t < TN; ++t) bs_sel[t] = sc.b[t] >> (8 * g);
+        for (int t = 0; t < TN; ++t) bs_sel[t] = sc.b[t] >> (8 * g);
+      }
 #pragma unroll
       for (int x = 0; x < TN; ++x)
 #pragma unroll
@@ -1099,11 +1123,11 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     if constexpr (!CHAIN) {
       asm volatile("" ::"v"(sc2[0].a));
 #pragma unroll
-      for (int t = 0; t < TN; ++t) asm volatile("" ::"v"(sc2[0].b[t]));
+      for (int t = 0; t < SBW; ++t) asm volatile("" ::"v"(sc2[0].b[t]));
     }
     asm volatile("" ::"v"(sc2[1].a));
 #pragma unroll
-    for (int t = 0; t < TN; ++t) asm volatile("" ::"v"(sc2[1].b[t]));
+    for (int t = 0; t < SBW; ++t) asm volatile("" ::"v"(sc2[1].b[t]));
 
     block_barrier();  // every wave's loads have landed and its reads are done
     int tid_e = tid;
