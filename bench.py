@@ -55,8 +55,8 @@ def _parse():
 # counter of a 1 GiB copy onto 1 GiB. Valid only for the kernel code it was taken on
 # (gemm_code_sha256).
 GEMM_TRAFFIC = {
-    "source_sha256": "a0d3950d521ca0b0bd6b3a2d5d63476df38fbb18ea9c03b4f53b25a80b6a9fc9",
-    "fetch_kib": 456460.8, "write_kib": 393302.7,
+    "source_sha256": "cfcfa873f8eecd7e4c84beeb6507e33015ad2fa03408e92d391dc60841b56e40",
+    "fetch_kib": 456989.6, "write_kib": 393301.5,
     "fetch_factor": 2.0, "write_factor": 1.0,
 }
 
