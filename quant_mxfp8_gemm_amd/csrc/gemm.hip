@@ -25,7 +25,8 @@
 //    output in whole 16-byte segments it, and the 256 x 192 tile, run as two wave groups that
 //    take turns on each SIMD's matrix pipe (one issues a half step's MFMAs from registers while
 //    the other reads its next fragments from LDS and issues the loads), with a barrier between
-//    turns (gemm_pingpong_bf16_kernel). Otherwise (the fused gate_up epilogue, unaligned output)
+//    turns (gemm_pingpong_bf16_kernel, which also serves the fused gate_up epilogue on 256 x 256
+//    tiles). Otherwise (unaligned output, the fused epilogue with inter not a multiple of 128)
 //    its A refill (and the refills of the staged tiles of up to 128 rows) is issued between
 //    the two 64-K halves of a step and its B refill after the step's MFMAs, so the step's
 //    first fragment reads and MFMAs follow the barrier at once. With at most 32 rows in one chunk (decode)
@@ -228,6 +229,83 @@ struct SwiGluOut {
 };
 
 enum { EPI_BF16 = 0, EPI_SWIGLU = 1 };
+
+// Fused dense GEMM1 epilogue of one tile (EPI_SWIGLU) from the accumulators of the wave at
+// (wm, wn): fp32 gate and up staged in LDS a band of rows at a time, then one (row, 32-block of j)
+// per thread: y = SiLU(g) * u, UE8M0 scale from amax, E4M3 codes. The caller makes sure nothing
+// else reads or writes the tile's LDS meanwhile.
+template <class T>
+__device__ __forceinline__ void swiglu_epilogue(uint8_t* smem, const v16f (&acc)[T::TN][T::TM], int wm, int wn,
+                                                int l32, int g, int tid, int m0, int m_end, int n0,
+                                                const SwiGluOut& sg) {
+  constexpr int BM = T::BM, BN = T::BN, HB = BN / 2;
+  // ---- fused epilogue: fp32 gate and up staged in LDS a band of rows at a time, then one
+  // (row, 32-block of j) per thread: y = SiLU(g) * u, UE8M0 scale from amax, E4M3 codes
+  // Bytes per staged row (gate floats, then up floats). A staged column c sits at
+  // c ^ 16 where bit 6 of c is set: the readers below take 16 rows x 4 blocks of 32 columns
+  // at a time, and without it blocks b and b + 2 of a row would share their banks.
+  constexpr int SROW = BN * 4 + 16;
+  constexpr int FIT = T::LDS_BYTES / SROW / 32 * 32;
+  constexpr int PR = FIT < BM ? FIT : BM;  // rows per band
+  static_assert(PR >= 32 && BM % PR == 0 && T::WTM % 32 == 0, "fused epilogue bands");
+  constexpr int BPR = HB / 32;  // 32-blocks of j per tile row
+  const int nblk = sg.inter / 32;
+  const int64_t col_tiles = (nblk + 3) / 4;
+#pragma unroll
+  for (int p0 = 0; p0 < BM; p0 += PR) {
+    block_barrier();  // the stages (or the previous band) are no longer read
+#pragma unroll
+    for (int y = 0; y < T::TM; ++y) {
+      const int rb = wm * T::WTM + y * 32;
+      if (rb < p0 || rb >= p0 + PR) continue;
+      const int r = rb - p0 + l32;
+#pragma unroll
+      for (int x = 0; x < T::TN; ++x)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = wn * T::WTN + x * 32 + 8 * q + 4 * g;
+          *(float4*)(smem + r * SROW + (c ^ (((c >> 6) & 1) << 4)) * 4) =
+              make_float4(acc[x][y][4 * q + 0], acc[x][y][4 * q + 1], acc[x][y][4 * q + 2], acc[x][y][4 * q + 3]);
+        }
+    }
+    block_barrier();
+    for (int it = tid; it < PR * BPR; it += T::NT) {
+      const int r = it / BPR, b = it % BPR;
+      const int m = m0 + p0 + r;
+      const int j = n0 + 32 * b;
+      if (m >= m_end || j >= sg.inter) continue;
+      const float* gp = (const float*)(smem + r * SROW) + 32 * b;
+      const float* up = gp + HB;
+      const int xg = ((32 * b) & 64) >> 2, xu = ((32 * b + HB) & 64) >> 2;  // the column swizzle
+      float yv[32];
+      uint32_t amax = 0;
+#pragma unroll
+      for (int e = 0; e < 32; e += 4) {
+        const float4 g4 = *(const float4*)(gp + (e ^ xg));
+        const float4 u4 = *(const float4*)(up + (e ^ xu));
+        const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+        const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float v = gg[t] / (1.0f + expf(-gg[t])) * uu[t];
+          yv[e + t] = v;
+          amax = max(amax, __float_as_uint(v) & 0x7FFFFFFFu);
+        }
+      }
+      const uint32_t code = ue8m0_from_amax_f32_bits(amax);
+      const float inv = inv_scale_from_ue8m0(code);
+      uint32_t w[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        w[t] = cvt_e4m3x4(yv[4 * t] * inv, yv[4 * t + 1] * inv, yv[4 * t + 2] * inv, yv[4 * t + 3] * inv);
+      uint8_t* qd = sg.q + (int64_t)m * sg.inter + j;
+      __builtin_nontemporal_store((u32x4){w[0], w[1], w[2], w[3]}, (u32x4*)qd);
+      __builtin_nontemporal_store((u32x4){w[4], w[5], w[6], w[7]}, (u32x4*)(qd + 16));
+      if (sg.s_lin) sg.s_lin[(int64_t)m * nblk + j / 32] = (uint8_t)code;
+      if (sg.s_swz) sg.s_swz[swizzled_offset(m, j / 32, col_tiles)] = (uint8_t)code;
+    }
+  }
+}
 
 template <class T, int A_LAYOUT, int B_LAYOUT, int EPI>
 __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
@@ -550,72 +628,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
     }  // main loop
 
     if constexpr (EPI == EPI_SWIGLU) {
-      // ---- fused epilogue: fp32 gate and up staged in LDS a band of rows at a time, then one
-      // (row, 32-block of j) per thread: y = SiLU(g) * u, UE8M0 scale from amax, E4M3 codes
-      // Bytes per staged row (gate floats, then up floats). A staged column c sits at
-      // c ^ 16 where bit 6 of c is set: the readers below take 16 rows x 4 blocks of 32 columns
-      // at a time, and without it blocks b and b + 2 of a row would share their banks.
-      constexpr int SROW = BN * 4 + 16;
-      constexpr int FIT = T::LDS_BYTES / SROW / 32 * 32;
-      constexpr int PR = FIT < BM ? FIT : BM;  // rows per band
-      static_assert(PR >= 32 && BM % PR == 0 && T::WTM % 32 == 0, "fused epilogue bands");
-      constexpr int BPR = HB / 32;  // 32-blocks of j per tile row
-      const int nblk = sg.inter / 32;
-      const int64_t col_tiles = (nblk + 3) / 4;
-#pragma unroll
-      for (int p0 = 0; p0 < BM; p0 += PR) {
-        block_barrier();  // the stages (or the previous band) are no longer read
-#pragma unroll
-        for (int y = 0; y < T::TM; ++y) {
-          const int rb = wm * T::WTM + y * 32;
-          if (rb < p0 || rb >= p0 + PR) continue;
-          const int r = rb - p0 + l32;
-#pragma unroll
-          for (int x = 0; x < T::TN; ++x)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int c = wn * T::WTN + x * 32 + 8 * q + 4 * g;
-              *(float4*)(smem + r * SROW + (c ^ (((c >> 6) & 1) << 4)) * 4) =
-                  make_float4(acc[x][y][4 * q + 0], acc[x][y][4 * q + 1], acc[x][y][4 * q + 2], acc[x][y][4 * q + 3]);
-            }
-        }
-        block_barrier();
-        for (int it = tid; it < PR * BPR; it += T::NT) {
-          const int r = it / BPR, b = it % BPR;
-          const int m = m0 + p0 + r;
-          const int j = n0 + 32 * b;
-          if (m >= m_end || j >= sg.inter) continue;
-          const float* gp = (const float*)(smem + r * SROW) + 32 * b;
-          const float* up = gp + HB;
-          const int xg = ((32 * b) & 64) >> 2, xu = ((32 * b + HB) & 64) >> 2;  // the column swizzle
-          float yv[32];
-          uint32_t amax = 0;
-#pragma unroll
-          for (int e = 0; e < 32; e += 4) {
-            const float4 g4 = *(const float4*)(gp + (e ^ xg));
-            const float4 u4 = *(const float4*)(up + (e ^ xu));
-            const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
-            const float uu[4] = {u4.x, u4.y, u4.z, u4.w};
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              const float v = gg[t] / (1.0f + expf(-gg[t])) * uu[t];
-              yv[e + t] = v;
-              amax = max(amax, __float_as_uint(v) & 0x7FFFFFFFu);
-            }
-          }
-          const uint32_t code = ue8m0_from_amax_f32_bits(amax);
-          const float inv = inv_scale_from_ue8m0(code);
-          uint32_t w[8];
-#pragma unroll
-          for (int t = 0; t < 8; ++t)
-            w[t] = cvt_e4m3x4(yv[4 * t] * inv, yv[4 * t + 1] * inv, yv[4 * t + 2] * inv, yv[4 * t + 3] * inv);
-          uint8_t* qd = sg.q + (int64_t)m * sg.inter + j;
-          __builtin_nontemporal_store((u32x4){w[0], w[1], w[2], w[3]}, (u32x4*)qd);
-          __builtin_nontemporal_store((u32x4){w[4], w[5], w[6], w[7]}, (u32x4*)(qd + 16));
-          if (sg.s_lin) sg.s_lin[(int64_t)m * nblk + j / 32] = (uint8_t)code;
-          if (sg.s_swz) sg.s_swz[swizzled_offset(m, j / 32, col_tiles)] = (uint8_t)code;
-        }
-      }
+      swiglu_epilogue<T>(smem, acc, wm, wn, l32, g, tid, m0, m_end, n0, sg);
       continue;  // next tile (the fused output has no chunk counters)
     }
 
@@ -701,18 +714,23 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
 //    are dropped), so every wave issues the same 16 stores, and the next tile's first waits let
 //    exactly those stay in flight. 256 x 192 (two tiles per compute unit at most, for the
 //    M = 2048-4096 workloads): the whole tile is staged once the loads have landed.
-template <class T, int CH>
+template <class T, int CH, int EPI = EPI_BF16>
 __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, uint16_t* __restrict__ C, int M, int N, int K, int ldc, int num_chunks,
-    int first_chunk, int* __restrict__ chunk_done) {
+    int first_chunk, int* __restrict__ chunk_done, SwiGluOut sg = SwiGluOut{}) {
   constexpr int BM = T::BM, BN = T::BN;
+  // EPI_SWIGLU (fused dense GEMM1, 256 x 256 only): a tile's columns are HB gate columns j0.. and
+  // the HB up columns of the same j (B rows j0.. and inter + j0..; inter a multiple of HB,
+  // checked by the caller), and its epilogue writes E4M3 codes and scales of SiLU(gate) * up
+  constexpr int HB = BN / 2;
+  static_assert(EPI == EPI_BF16 || (BN == 256 && CH == 0), "fused epilogue: 256 x 256, unchained");
   static_assert(T::SPLIT && BM == 256 && (BN == 256 || BN == 192) && T::TM == 2 && T::NT == 512 &&
                     T::DA == 4 && T::WTM == 64 && T::A_BYTES == 32768 && T::WTN == BN / 2,
                 "256-row tiles of 8 waves of 64 x BN/2");
   constexpr int TN = T::TN;
   // overlapped epilogue (quarters through A slot 1 and B slot 2): 256 x 256
-  constexpr bool OVL = BN == 256;
+  constexpr bool OVL = BN == 256 && EPI == EPI_BF16;
   // B slots at 0, 1 and 2 B_BYTES, A slots after them
   constexpr int B_RING = 0, A_RING = 3 * T::B_BYTES;
   static_assert(A_RING + 2 * T::A_BYTES <= 160 * 1024, "ring");
@@ -736,7 +754,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
   const int g = lane >> 5;
 
   const int chunk_rows = M / num_chunks;
-  const int tiles_n = (N + BN - 1) / BN;
+  const int tiles_n = EPI == EPI_SWIGLU ? sg.inter / HB : (N + BN - 1) / BN;
   const int tiles_mc = (chunk_rows + BM - 1) / BM;
   const int tpc = tiles_mc * tiles_n;
   const int total = tpc * num_chunks;
@@ -769,7 +787,7 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     const int chunk_m0 = ts.chunk * chunk_rows;
     ts.m0 = chunk_m0 + tm_idx * BM;
     ts.m_end = min(ts.m0 + BM, chunk_m0 + chunk_rows);
-    ts.n0 = tn_idx * BN;
+    ts.n0 = tn_idx * (EPI == EPI_SWIGLU ? HB : BN);
     // lane terms from an opaque copy of the lane index: recomputed per tile rather than kept
     // live through the main loop
     int ln = lane;
@@ -786,7 +804,9 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     for (int i = 0; i < T::DB; ++i) {
       const int sidx = (wave * T::DB + i) * 64 + ln;
       const int r = sidx >> 3;
-      ts.b_off[i] = (uint32_t)min(ts.n0 + r, N - 1) * (uint32_t)K + (((sidx & 7) ^ swz(r)) * 16);
+      const uint32_t brow = EPI == EPI_SWIGLU ? (uint32_t)(r < HB ? ts.n0 + r : sg.inter + ts.n0 + (r - HB))
+                                              : (uint32_t)min(ts.n0 + r, N - 1);
+      ts.b_off[i] = brow * (uint32_t)K + (((sidx & 7) ^ swz(r)) * 16);
     }
     // rows r, r + 32, r + 64, r + 96 of a swizzled 128-row group keep their 4-byte scale groups
     // side by side: one 8-byte load for the wave's two A row blocks, one 16-byte load for the
@@ -794,7 +814,8 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     // the three blocks of a 96-column wave touch (rows past the operand read zero padding or 0;
     // not stored)
     ts.sa_off = scale_base<1>((uint32_t)(ts.m0 + wm * T::WTM + (ln & 31)), nblk4);
-    const uint32_t c0 = (uint32_t)(ts.n0 + wn * T::WTN);  // a multiple of 32
+    // the wave's first B row (a multiple of 32; fused: its 128 gate or up rows)
+    const uint32_t c0 = EPI == EPI_SWIGLU ? (uint32_t)(wn == 0 ? ts.n0 : sg.inter + ts.n0) : (uint32_t)(ts.n0 + wn * T::WTN);
     ts.sbq = (int)(c0 >> 5) & 3;
     if constexpr (SB_TWO_GROUPS)  // past the last group the load reads 0 (resource bound)
       ts.sb_off[0] = scale_base<1>(((c0 >> 7) + (uint32_t)(ln >> 5)) * 128 + (uint32_t)(ln & 31), nblk4);
@@ -1134,7 +1155,15 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     asm volatile("" : "+v"(tid_e));
     const int e32 = tid_e & 31, eg = (tid_e >> 5) & 1;
     const int nbid = bid + (int)gridDim.x;
-    if constexpr (OVL) {
+    if constexpr (EPI == EPI_SWIGLU) {
+      // every load has landed (unchained); the fused epilogue stages through the whole LDS
+      swiglu_epilogue<T>(smem, acc, wm, wn, e32, eg, tid_e, done_m0, done_m_end, done_n0, sg);
+      if (has_next) {
+        block_barrier();  // every wave has read its part of the staged band
+        setup(nbid, cur);
+        first_loads(cur, sc2[0]);
+      }
+    } else if constexpr (OVL) {
       // ---- epilogue, with the next tile's first loads issued half-way.
       // Quarter qd = (y, h): tile rows 64 wm + 32 y + [0, 32) of every wm and tile columns
       // 128 wn + 64 h + [0, 64) of both wn, staged as 128 rows of 256 bytes (row 32 wm + l32,
@@ -1362,32 +1391,43 @@ bool split_ring_fits(const uint8_t* as, int a_layout, const uint8_t* bs, int b_l
 // The two-group BF16 kernel (swizzled, 16-byte aligned scales on 64-row chunk boundaries, checked
 // by the caller): output in whole 16-byte segments, at least two K steps, tile offsets in 32
 // bits. Returns false (launching nothing) when the output does not qualify.
-template <class T>
+template <class T, int EPI = EPI_BF16>
 bool launch_two_group(const uint8_t* a, const uint8_t* as, const uint8_t* b, const uint8_t* bs, int64_t m, int64_t n,
                       int64_t k, uint16_t* c, int64_t ldc, int num_chunks, int first_chunk, int* chunk_done,
-                      hipStream_t stream, hipError_t& err) {
-  const bool wide = (uintptr_t)c % 16 == 0 && ldc % 8 == 0;
-  if (!(k >= 2 * BK && n % 8 == 0 && wide && (int64_t)ldc * 2 * T::BM < (1ll << 31))) return false;
-  const int64_t tiles = tile_count(m, n, num_chunks, T::BM, T::BN);
-  const int64_t grid = tiles < device_cu_count() ? tiles : device_cu_count();
-  // with the overlapped epilogue and an even number of K steps, consecutive tiles chain their
-  // loads; the variant follows the number of steps after the last whole group of six
-  const int kt = (int)(k / BK);
-  constexpr int CH5 = T::BN == 256 ? 5 : 0, CH3 = T::BN == 256 ? 3 : 0, CH1 = T::BN == 256 ? 1 : 0;
-  if (T::BN == 256 && kt % 6 == 0)
-    gemm_pingpong_bf16_kernel<T, CH5><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
-        a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
-  else if (T::BN == 256 && kt % 6 == 4)
-    gemm_pingpong_bf16_kernel<T, CH3><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
-        a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
-  else if (T::BN == 256 && kt % 6 == 2)
-    gemm_pingpong_bf16_kernel<T, CH1><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
-        a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
-  else
-    gemm_pingpong_bf16_kernel<T, 0><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
-        a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
-  err = hipGetLastError();
-  return true;
+                      hipStream_t stream, hipError_t& err, SwiGluOut sg = SwiGluOut{}) {
+  if constexpr (EPI == EPI_SWIGLU) {
+    // fused dense GEMM1: 256 x 256 tiles of 128 gate and 128 up columns, no chunk counters
+    if (!(T::BN == 256 && k >= 2 * BK && sg.inter % 128 == 0 && n == 2 * (int64_t)sg.inter)) return false;
+    const int64_t tiles = tile_count(m, sg.inter * 2, num_chunks, T::BM, T::BN);
+    const int64_t grid = tiles < device_cu_count() ? tiles : device_cu_count();
+    gemm_pingpong_bf16_kernel<T, 0, EPI_SWIGLU><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
+        a, as, b, bs, nullptr, (int)m, (int)n, (int)k, 0, num_chunks, first_chunk, nullptr, sg);
+    err = hipGetLastError();
+    return true;
+  } else {
+    const bool wide = (uintptr_t)c % 16 == 0 && ldc % 8 == 0;
+    if (!(k >= 2 * BK && n % 8 == 0 && wide && (int64_t)ldc * 2 * T::BM < (1ll << 31))) return false;
+    const int64_t tiles = tile_count(m, n, num_chunks, T::BM, T::BN);
+    const int64_t grid = tiles < device_cu_count() ? tiles : device_cu_count();
+    // with the overlapped epilogue and an even number of K steps, consecutive tiles chain their
+    // loads; the variant follows the number of steps after the last whole group of six
+    const int kt = (int)(k / BK);
+    constexpr int CH5 = T::BN == 256 ? 5 : 0, CH3 = T::BN == 256 ? 3 : 0, CH1 = T::BN == 256 ? 1 : 0;
+    if (T::BN == 256 && kt % 6 == 0)
+      gemm_pingpong_bf16_kernel<T, CH5><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
+          a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
+    else if (T::BN == 256 && kt % 6 == 4)
+      gemm_pingpong_bf16_kernel<T, CH3><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
+          a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
+    else if (T::BN == 256 && kt % 6 == 2)
+      gemm_pingpong_bf16_kernel<T, CH1><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
+          a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
+    else
+      gemm_pingpong_bf16_kernel<T, 0><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
+          a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done);
+    err = hipGetLastError();
+    return true;
+  }
 }
 
 template <int EPI>
@@ -1401,6 +1441,9 @@ hipError_t launch_split(const uint8_t* a, const uint8_t* as, const uint8_t* b, c
   hipError_t err = hipSuccess;
   if (EPI == EPI_BF16 &&
       launch_two_group<T>(a, as, b, bs, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream, err))
+    return err;
+  if (EPI == EPI_SWIGLU && num_chunks == 1 &&
+      launch_two_group<T, EPI_SWIGLU>(a, as, b, bs, m, n, k, nullptr, 0, 1, 0, nullptr, stream, err, sg))
     return err;
   gemm_kernel<T, 1, 1, EPI><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
       a, as, b, bs, c, (int)m, (int)n, (int)k, (int)ldc, num_chunks, first_chunk, chunk_done, wide, sg);
