@@ -26,10 +26,10 @@
 //    take turns on each SIMD's matrix pipe (one issues a half step's MFMAs from registers while
 //    the other reads its next fragments from LDS and issues the loads), with a barrier between
 //    turns (gemm_pingpong_bf16_kernel, which also serves the fused gate_up epilogue on 256 x 256
-//    tiles). Otherwise (unaligned BF16 output, a single 128-K step) its A refill (and the refills of the staged tiles of up to 128 rows) is issued between
-//    the two 64-K halves of a step and its B refill after the step's MFMAs, so the step's
-//    first fragment reads and MFMAs follow the barrier at once. With at most 32 rows in one chunk (decode)
-//    the BF16 GEMM uses one-wave 32 x 32 tiles whose fragments and scales go straight from memory
+//    tiles). Otherwise (unaligned BF16 output, a single 128-K step) its A refill (and the
+//    refills of the staged tiles of up to 128 rows) is issued between the two 64-K halves of a
+//    step and its B refill after the step's MFMAs, so the step's first fragment reads and MFMAs
+//    follow the barrier at once. With at most 32 rows in one chunk (decode) the BF16 GEMM uses one-wave 32 x 32 tiles whose fragments and scales go straight from memory
 //    into registers, eight K steps ahead, with no LDS stages or barriers. Every other case uses
 //    NS-stage buffers holding A, B and the scale dwords together. All give the same bits:
 //    every configuration sums the same MFMA partials in the same order.
