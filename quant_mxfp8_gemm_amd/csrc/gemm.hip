@@ -244,8 +244,9 @@ __device__ __forceinline__ void swiglu_epilogue(uint8_t* smem, const v16f (&acc)
   // c ^ 16 where bit 6 of c is set: the readers below take 16 rows x 4 blocks of 32 columns
   // at a time, and without it blocks b and b + 2 of a row would share their banks.
   constexpr int SROW = BN * 4 + 16;
-  constexpr int FIT = T::LDS_BYTES / SROW / 32 * 32;
-  constexpr int PR = FIT < BM ? FIT : BM;  // rows per band
+  constexpr int FIT = T::LDS_BYTES / SROW;
+  // rows per band: the whole tile, else half or a quarter of it, whatever fits
+  constexpr int PR = FIT >= BM ? BM : FIT >= BM / 2 ? BM / 2 : BM / 4;
   static_assert(PR >= 32 && BM % PR == 0 && T::WTM % 32 == 0, "fused epilogue bands");
   constexpr int BPR = HB / 32;  // 32-blocks of j per tile row
   const int nblk = sg.inter / 32;
@@ -719,11 +720,11 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     const uint8_t* __restrict__ Bs, uint16_t* __restrict__ C, int M, int N, int K, int ldc, int num_chunks,
     int first_chunk, int* __restrict__ chunk_done, SwiGluOut sg = SwiGluOut{}) {
   constexpr int BM = T::BM, BN = T::BN;
-  // EPI_SWIGLU (fused dense GEMM1, 256 x 256 only): a tile's columns are HB gate columns j0.. and
-  // the HB up columns of the same j (B rows j0.. and inter + j0..; inter a multiple of HB,
-  // checked by the caller), and its epilogue writes E4M3 codes and scales of SiLU(gate) * up
+  // EPI_SWIGLU (fused dense GEMM1): a tile's columns are HB gate columns j0.. and the HB up
+  // columns of the same j (B rows j0.. and inter + j0..; inter a multiple of HB, checked by the
+  // caller), and its epilogue writes E4M3 codes and scales of SiLU(gate) * up
   constexpr int HB = BN / 2;
-  static_assert(EPI == EPI_BF16 || (BN == 256 && CH == 0), "fused epilogue: 256 x 256, unchained");
+  static_assert(EPI == EPI_BF16 || CH == 0, "fused epilogue: unchained");
   static_assert(T::SPLIT && BM == 256 && (BN == 256 || BN == 192) && T::TM == 2 && T::NT == 512 &&
                     T::DA == 4 && T::WTM == 64 && T::A_BYTES == 32768 && T::WTN == BN / 2,
                 "256-row tiles of 8 waves of 64 x BN/2");
@@ -1395,8 +1396,8 @@ bool launch_two_group(const uint8_t* a, const uint8_t* as, const uint8_t* b, con
                       int64_t k, uint16_t* c, int64_t ldc, int num_chunks, int first_chunk, int* chunk_done,
                       hipStream_t stream, hipError_t& err, SwiGluOut sg = SwiGluOut{}) {
   if constexpr (EPI == EPI_SWIGLU) {
-    // fused dense GEMM1: 256 x 256 tiles of 128 gate and 128 up columns, no chunk counters
-    if (!(T::BN == 256 && k >= 2 * BK && sg.inter % 128 == 0 && n == 2 * (int64_t)sg.inter)) return false;
+    // fused dense GEMM1: tiles of BN / 2 gate and BN / 2 up columns, no chunk counters
+    if (!(k >= 2 * BK && sg.inter % (T::BN / 2) == 0 && n == 2 * (int64_t)sg.inter)) return false;
     const int64_t tiles = tile_count(m, sg.inter * 2, num_chunks, T::BM, T::BN);
     const int64_t grid = tiles < device_cu_count() ? tiles : device_cu_count();
     gemm_pingpong_bf16_kernel<T, 0, EPI_SWIGLU><<<dim3((unsigned)grid), dim3(T::NT), 0, stream>>>(
@@ -1478,7 +1479,11 @@ hipError_t launch_gemm_silu_mul_quant(const uint8_t* a, const uint8_t* as, int a
       else
         e = launch_cfg<TileL, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg);
       break;
-    case CFG_N: e = launch_cfg<TileN, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
+    case CFG_N:
+      if (!(split_ring_fits(as, a_layout, ws, w_layout, m, 1) &&
+            launch_two_group<TileNR, EPI_SWIGLU>(a, as, w, ws, m, n, k, nullptr, 0, 1, 0, nullptr, stream, e, sg)))
+        e = launch_cfg<TileN, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg);
+      break;
     case CFG_Q: e = launch_cfg<TileQ, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
     case CFG_R: e = launch_cfg<TileR, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;
     case CFG_W: e = launch_cfg<TileW, EPI_SWIGLU>(a, as, a_layout, w, ws, w_layout, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg); break;

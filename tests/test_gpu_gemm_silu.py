@@ -109,13 +109,14 @@ def test_gemm_silu_mul_quant_workload_rows():
         assert np.array_equal(s_swz[offs], s_lin[r])
 
 
-@pytest.mark.parametrize("m,inter,k", [(2048, 3072, 640), (2048, 6144, 384)])
-def test_gemm_silu_mul_quant_split_ring_matches_staged(m, inter, k):
-    """With 256 x 256 tiles and swizzled, 16-byte aligned scales the kernel runs as two wave
-    groups (B three stages deep, the scales in registers; 384 tiles in the second case, so some
-    workgroups take two); scale buffers 4 bytes off that alignment take the staged kernel. Both
-    form the same fp32 sums, so codes and scales agree bit for bit (and with the oracle's within
-    the accumulation bound, checked on the first case)."""
+@pytest.mark.parametrize("m,inter,k,tile_n", [(2048, 3072, 640, 192), (2048, 6144, 384, 192), (8192, 3072, 384, 256)])
+def test_gemm_silu_mul_quant_split_ring_matches_staged(m, inter, k, tile_n):
+    """With swizzled, 16-byte aligned scales the 256 x 192 and 256 x 256 tiles run as two wave
+    groups (B three stages deep, the scales in registers; 512 and 768 tiles in the last two
+    cases, so workgroups take two or three); scale buffers 4 bytes off that alignment take the
+    staged kernel. Both form the same fp32 sums, so codes and scales agree bit for bit (and with
+    the oracle's within the accumulation bound, checked on the first case)."""
+    assert mx.gemm_tiles_per_chunk(m, 2 * inter, 1) == ((m + 255) // 256) * (2 * inter // tile_n)
     print(f"fused GEMM1 two-group vs staged m={m} inter={inter} k={k}", flush=True)
     qa, sa, qw, sw = _operands(m, inter, k, seed_a=11, seed_w=12)
     outs = []
@@ -132,7 +133,7 @@ def test_gemm_silu_mul_quant_split_ring_matches_staged(m, inter, k):
         outs.append((q.cpu().numpy(), s_lin.cpu().numpy(), s_swz.cpu().numpy()))
     for x, y in zip(*outs):
         assert np.array_equal(x, y)
-    if inter != 3072:
+    if (m, inter) != (2048, 3072):
         return
     q_ref, s_ref, _, gu = oracle.gemm_silu_mul_quant(qa, sa[1], 1, qw, sw[1], 1, want_gu=True)
     mass = _mass(qa, sa[1], 1, qw, sw[1], 1, range(m))
