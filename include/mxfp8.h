@@ -185,7 +185,8 @@ int mxfp8_swizzle_scales_check(const void* scales_linear, int64_t rows, int64_t 
  *   chunk_done NULL, or a device int array [num_chunks] that the caller zeroes before the
  *   call: after every output tile of chunk c has been stored and made visible device-wide,
  *   chunk_done[c] is incremented once per tile; the chunk is complete when it reaches
- *   mxfp8_gemm_tiles_per_chunk(m, n, num_chunks). This is the hook a reduce-scatter
+ *   mxfp8_gemm_tiles_per_chunk(m, n, num_chunks, a_scale_layout, b_scale_layout). This is
+ *   the hook a reduce-scatter
  *   would wait on.
  * The result does not depend on num_chunks, first_chunk or chunk_done.
  * Performance: large problems run fastest with both scale buffers in the swizzled layout,
@@ -233,9 +234,13 @@ int mxfp8_gemm_silu_mul_quant_check(const void* a_e4m3, const void* a_scales, in
                                     int64_t m, int64_t inter, int64_t k, const void* q_e4m3,
                                     const void* scales_linear, const void* scales_swizzled);
 
-/* Output tiles per chunk that mxfp8_gemm_bf16out uses for this shape (the final value of
- * each chunk_done counter); -1 for invalid arguments. Host-only. */
-int64_t mxfp8_gemm_tiles_per_chunk(int64_t m, int64_t n, int num_chunks);
+/* Output tiles per chunk that mxfp8_gemm_bf16out uses for this shape and these scale layouts
+ * (the final value of each chunk_done counter): the tile shape follows m, n, num_chunks and
+ * whether both scale buffers are swizzled (MXFP8_SCALES_SWIZZLED_128X4), not the buffers'
+ * addresses.
+ * -1 for invalid arguments. Host-only. */
+int64_t mxfp8_gemm_tiles_per_chunk(int64_t m, int64_t n, int num_chunks, int a_scale_layout,
+                                   int b_scale_layout);
 
 #ifdef __cplusplus
 }

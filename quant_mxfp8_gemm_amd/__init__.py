@@ -72,7 +72,7 @@ def load_library():
     lib.mxfp8_gemm_silu_mul_quant_check.restype = i32
     lib.mxfp8_gemm_silu_mul_quant_check.argtypes = [vp, vp, i32, vp, vp, i32, i64, i64, i64, vp, vp, vp]
     lib.mxfp8_gemm_tiles_per_chunk.restype = i64
-    lib.mxfp8_gemm_tiles_per_chunk.argtypes = [i64, i64, i32]
+    lib.mxfp8_gemm_tiles_per_chunk.argtypes = [i64, i64, i32, i32, i32]
     _lib = lib
     return lib
 
@@ -88,8 +88,9 @@ def scale_bytes(rows: int, k: int, layout: int) -> int:
     return n
 
 
-def gemm_tiles_per_chunk(m: int, n: int, num_chunks: int) -> int:
-    t = load_library().mxfp8_gemm_tiles_per_chunk(int(m), int(n), int(num_chunks))
+def gemm_tiles_per_chunk(m: int, n: int, num_chunks: int, a_layout: int, b_layout: int) -> int:
+    """Output tiles per chunk of ``gemm`` with these scale layouts (the final ``chunk_done`` value)."""
+    t = load_library().mxfp8_gemm_tiles_per_chunk(int(m), int(n), int(num_chunks), int(a_layout), int(b_layout))
     if t < 0:
         raise MXFP8Error("mxfp8_gemm_tiles_per_chunk", EINVAL)
     return t

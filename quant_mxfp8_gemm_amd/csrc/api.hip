@@ -80,9 +80,11 @@ int mxfp8_gemm_silu_mul_quant(const void* a_e4m3, const void* a_scales, int a_sc
       (uint8_t*)scales_swizzled, stream));
 }
 
-int64_t mxfp8_gemm_tiles_per_chunk(int64_t m, int64_t n, int num_chunks) {
+int64_t mxfp8_gemm_tiles_per_chunk(int64_t m, int64_t n, int num_chunks, int a_scale_layout,
+                                   int b_scale_layout) {
   if (m < 1 || n < 1 || num_chunks < 1 || m % num_chunks != 0) return -1;
-  const mxfp8::GemmShape s = mxfp8::gemm_pick_shape(m, n, num_chunks);
+  if ((a_scale_layout != 0 && a_scale_layout != 1) || (b_scale_layout != 0 && b_scale_layout != 1)) return -1;
+  const mxfp8::GemmShape s = mxfp8::gemm_pick_shape(m, n, num_chunks, a_scale_layout, b_scale_layout);
   return ((m / num_chunks + s.bm - 1) / s.bm) * ((n + s.bn - 1) / s.bn);
 }
 

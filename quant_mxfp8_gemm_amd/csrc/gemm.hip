@@ -1354,8 +1354,21 @@ int pick_config(int64_t m, int64_t n, int num_chunks) {
 // 8 rows x 128 bytes per instruction where a register load covers 32 rows x 32 bytes, and
 // the extra requests cost more than the barriers saved (M = 64: 16.8 against 14.1 us; M = 128
 // in four chunks of 32 rows: 20.9 against 12.1 us).
-int pick_config_bf16(int64_t m, int64_t n, int num_chunks) {
-  const int c = pick_config(m, n, num_chunks);
+//
+// With both scales swizzled (and chunks on 64-row boundaries) the 256 x 256 and 256 x 192 tiles
+// run the two-group kernel, whose K step costs less than the staged tiles' model assumes; where
+// the model picks the staged 192 x 192 tile and a chunk has at least 256 rows, the two-group
+// 256 x 192 tile is faster (M = 1536: 28.6 / 38.3 against 29.4 / 40.0 us at K = 2048 / 3072;
+// M = 3072: 48.9 / 68.5 against 54.4 / 76.4 us; 4 chunks, N = 6144). The choice depends on the
+// layouts only, not on the buffers' alignment, so that the tile count per chunk is known to the
+// caller beforehand (mxfp8_gemm_tiles_per_chunk).
+bool two_group_layouts(int a_layout, int b_layout, int64_t m, int num_chunks) {
+  return a_layout == 1 && b_layout == 1 && (num_chunks == 1 || (m / num_chunks) % 64 == 0);
+}
+
+int pick_config_bf16(int64_t m, int64_t n, int num_chunks, bool two_group) {
+  int c = pick_config(m, n, num_chunks);
+  if (two_group && c == CFG_Q && m / num_chunks >= 256) c = CFG_N;
   return c == CFG_T && num_chunks == 1 && m <= 32 ? CFG_D : c;
 }
 
@@ -1452,8 +1465,8 @@ hipError_t launch_split(const uint8_t* a, const uint8_t* as, const uint8_t* b, c
 
 }  // namespace
 
-GemmShape gemm_pick_shape(int64_t m, int64_t n, int num_chunks) {
-  switch (pick_config_bf16(m, n, num_chunks)) {
+GemmShape gemm_pick_shape(int64_t m, int64_t n, int num_chunks, int a_layout, int b_layout) {
+  switch (pick_config_bf16(m, n, num_chunks, two_group_layouts(a_layout, b_layout, m, num_chunks))) {
     case CFG_L: return GemmShape{TileL::BM, TileL::BN};
     case CFG_N: return GemmShape{TileN::BM, TileN::BN};
     case CFG_Q: return GemmShape{TileQ::BM, TileQ::BN};
@@ -1472,7 +1485,9 @@ hipError_t launch_gemm_silu_mul_quant(const uint8_t* a, const uint8_t* as, int a
   const SwiGluOut sg{q, s_lin, s_swz, (int)inter};
   const int64_t n = 2 * inter;  // B rows; tile counts match whenever inter is a multiple of BN/2
   hipError_t e;
-  switch (pick_config(m, n, 1)) {
+  int cfg = pick_config(m, n, 1);
+  if (two_group_layouts(a_layout, w_layout, m, 1) && cfg == CFG_Q && m >= 256) cfg = CFG_N;  // as for BF16
+  switch (cfg) {
     case CFG_L:
       if (split_ring_fits(as, a_layout, ws, w_layout, m, 1) && inter % 128 == 0)
         e = launch_split<EPI_SWIGLU>(a, as, w, ws, m, n, k, nullptr, 0, 1, 0, nullptr, stream, sg);
@@ -1499,7 +1514,7 @@ hipError_t launch_gemm_silu_mul_quant(const uint8_t* a, const uint8_t* as, int a
 hipError_t launch_gemm(const uint8_t* a, const uint8_t* as, int a_layout, const uint8_t* b,
                        const uint8_t* bs, int b_layout, int64_t m, int64_t n, int64_t k, uint16_t* c,
                        int64_t ldc, int num_chunks, int first_chunk, int* chunk_done, hipStream_t stream) {
-  switch (pick_config_bf16(m, n, num_chunks)) {
+  switch (pick_config_bf16(m, n, num_chunks, two_group_layouts(a_layout, b_layout, m, num_chunks))) {
     case CFG_L:
       if (split_ring_fits(as, a_layout, bs, b_layout, m, num_chunks))
         return launch_split<EPI_BF16>(a, as, b, bs, m, n, k, c, ldc, num_chunks, first_chunk, chunk_done, stream);

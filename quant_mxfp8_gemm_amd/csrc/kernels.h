@@ -27,7 +27,7 @@ struct GemmShape {
 };
 
 // Tile shape the GEMM uses for this problem.
-GemmShape gemm_pick_shape(int64_t m, int64_t n, int num_chunks);
+GemmShape gemm_pick_shape(int64_t m, int64_t n, int num_chunks, int a_layout, int b_layout);
 
 hipError_t launch_gemm(const uint8_t* a, const uint8_t* as, int a_layout, const uint8_t* b,
                        const uint8_t* bs, int b_layout, int64_t m, int64_t n, int64_t k, uint16_t* c,

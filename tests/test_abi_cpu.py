@@ -169,25 +169,36 @@ def test_gemm_silu_mul_quant_check(lib):
 
 
 def test_tiles_per_chunk(lib):
-    t = mx.gemm_tiles_per_chunk(32768, 6144, 4)
+    """Tile counts per chunk (linear scales unless stated): the tile follows m, n, the chunking
+    and, where the two-group kernel applies, the scale layouts."""
+    t = mx.gemm_tiles_per_chunk(32768, 6144, 4, 0, 0)
     assert t > 0 and t * 4 * 256 * 256 >= 32768 * 6144
-    assert lib.mxfp8_gemm_tiles_per_chunk(10, 10, 3) == -1
+    assert lib.mxfp8_gemm_tiles_per_chunk(10, 10, 3, 0, 0) == -1
+    assert lib.mxfp8_gemm_tiles_per_chunk(32, 32, 1, 2, 0) == -1   # no such scale layout
     # the tile shrinks when a 256 x 256 tiling leaves the compute units idle
-    assert mx.gemm_tiles_per_chunk(32768, 6144, 4) == 32 * 24    # 256 x 256
-    assert mx.gemm_tiles_per_chunk(1024, 6144, 4) == 2 * 32      # 128 x 192: one full round
-    assert mx.gemm_tiles_per_chunk(512, 6144, 4) == 1 * 48       # 128 x 128
-    assert mx.gemm_tiles_per_chunk(128, 6144, 1) == 4 * 48       # 32 x 128
-    assert mx.gemm_tiles_per_chunk(128, 6144, 4) == 1 * 48       # 32 x 128
-    assert mx.gemm_tiles_per_chunk(33, 6144, 1) == 2 * 48
-    assert mx.gemm_tiles_per_chunk(32, 6144, 1) == 192           # 32 x 32, register-loaded
-    assert mx.gemm_tiles_per_chunk(1, 6144, 1) == 192
-    assert mx.gemm_tiles_per_chunk(32, 6144, 2) == 48            # 32 x 128 (two chunks)
-    assert mx.gemm_tiles_per_chunk(4096, 6144, 4) == 4 * 32      # 256 x 192: two full rounds
-    assert mx.gemm_tiles_per_chunk(3072, 6144, 4) == 4 * 32      # 192 x 192: 768 rows per chunk, no empty rows
-    assert mx.gemm_tiles_per_chunk(3000, 6144, 4) == 4 * 32      # 192 x 192 (256 x 192 would give 3 x 32)
-    assert mx.gemm_tiles_per_chunk(700, 6144, 4) == 2 * 32       # 96 x 192 for 175 rows (128 x 128 would give 2 x 48)
-    assert mx.gemm_tiles_per_chunk(256, 6144, 1) == 4 * 48       # 64 x 128
-    assert mx.gemm_tiles_per_chunk(128, 6144, 1) == 4 * 48       # 32 x 128
+    assert mx.gemm_tiles_per_chunk(32768, 6144, 4, 0, 0) == 32 * 24    # 256 x 256
+    assert mx.gemm_tiles_per_chunk(1024, 6144, 4, 0, 0) == 2 * 32      # 128 x 192: one full round
+    assert mx.gemm_tiles_per_chunk(512, 6144, 4, 0, 0) == 1 * 48       # 128 x 128
+    assert mx.gemm_tiles_per_chunk(128, 6144, 1, 0, 0) == 4 * 48       # 32 x 128
+    assert mx.gemm_tiles_per_chunk(128, 6144, 4, 0, 0) == 1 * 48       # 32 x 128
+    assert mx.gemm_tiles_per_chunk(33, 6144, 1, 0, 0) == 2 * 48
+    assert mx.gemm_tiles_per_chunk(32, 6144, 1, 0, 0) == 192           # 32 x 32, register-loaded
+    assert mx.gemm_tiles_per_chunk(1, 6144, 1, 0, 0) == 192
+    assert mx.gemm_tiles_per_chunk(32, 6144, 2, 0, 0) == 48            # 32 x 128 (two chunks)
+    assert mx.gemm_tiles_per_chunk(4096, 6144, 4, 0, 0) == 4 * 32      # 256 x 192: two full rounds
+    assert mx.gemm_tiles_per_chunk(3072, 6144, 4, 0, 0) == 4 * 32      # 192 x 192: 768 rows per chunk, no empty rows
+    assert mx.gemm_tiles_per_chunk(3000, 6144, 4, 0, 0) == 4 * 32      # 192 x 192 (256 x 192 would give 3 x 32)
+    assert mx.gemm_tiles_per_chunk(700, 6144, 4, 0, 0) == 2 * 32       # 96 x 192 for 175 rows (128 x 128 would give 2 x 48)
+    assert mx.gemm_tiles_per_chunk(256, 6144, 1, 0, 0) == 4 * 48       # 64 x 128
+    assert mx.gemm_tiles_per_chunk(128, 6144, 1, 0, 0) == 4 * 48       # 32 x 128
+    # both scales swizzled, chunks on 64-row boundaries: the two-group 256 x 192 tile replaces
+    # the staged 192 x 192 one once a chunk has 256 rows
+    assert mx.gemm_tiles_per_chunk(3072, 6144, 4, 1, 1) == 3 * 32    # 256 x 192
+    assert mx.gemm_tiles_per_chunk(3072, 6144, 4, 0, 1) == 4 * 32    # 192 x 192 (one linear)
+    assert mx.gemm_tiles_per_chunk(1536, 6144, 4, 1, 1) == 2 * 32    # 256 x 192 over 384 rows
+    assert mx.gemm_tiles_per_chunk(3000, 6144, 4, 1, 1) == 4 * 32    # 750-row chunks: staged
+    assert mx.gemm_tiles_per_chunk(32768, 6144, 4, 1, 1) == 32 * 24  # 256 x 256 either way
+    assert mx.gemm_tiles_per_chunk(1024, 6144, 4, 1, 1) == 2 * 32    # 128 x 192 either way
 
 
 # ---- the Python binding's own buffer checks (the C ABI cannot see buffer sizes)

@@ -124,7 +124,7 @@ TILE_CASES = [(2000, 8000, 256, 1, 256, 256), (1000, 12200, 256, 1, 256, 192), (
 def test_gemm_tile_configs_full(m, n, k, chunks, tm, tn, la, lb):
     print(f"gemm tile config {tm}x{tn}: m={m} n={n} k={k} chunks={chunks} layouts={la}{lb}", flush=True)
     rows = m // chunks
-    assert mx.gemm_tiles_per_chunk(m, n, chunks) == -(-rows // tm) * -(-n // tn)
+    assert mx.gemm_tiles_per_chunk(m, n, chunks, la, lb) == -(-rows // tm) * -(-n // tn)
     qa, sa, qb, sb = _operands(m, n, k, seed_a=m + 1, seed_b=n + 1)
     ref = oracle.gemm(qa, sa[la], la, qb, sb[lb], lb)
     c = _gpu_gemm(qa, sa[la], la, qb, sb[lb], lb, num_chunks=chunks, first_chunk=chunks - 1)
@@ -143,7 +143,7 @@ SPLIT_CASES = [(1984, 8000, 256, 1), (1984, 8000, 384, 1), (3968, 8000, 1152, 2)
 def test_gemm_split_ring_full(m, n, k, chunks):
     print(f"gemm split ring m={m} n={n} k={k} chunks={chunks}", flush=True)
     rows = m // chunks
-    assert mx.gemm_tiles_per_chunk(m, n, chunks) == -(-rows // 256) * -(-n // 256)
+    assert mx.gemm_tiles_per_chunk(m, n, chunks, 1, 1) == -(-rows // 256) * -(-n // 256)
     qa, sa, qb, sb = _operands(m, n, k, seed_a=k, seed_b=k + 1)
     ref = oracle.gemm(qa, sa[1], 1, qb, sb[1], 1)
     c = _gpu_gemm(qa, sa[1], 1, qb, sb[1], 1, num_chunks=chunks, first_chunk=chunks - 1)
@@ -306,7 +306,7 @@ def test_gemm_split_ring_overlapped_epilogue(k):
     c_ovl = _gpu_gemm(qa, sa[1], 1, qb, sb[1], 1, num_chunks=chunks, first_chunk=1, chunk_done=done, pad_cols=8)
     c_plain = _gpu_gemm(qa, sa[1], 1, qb, sb[1], 1, num_chunks=chunks, first_chunk=1, pad_cols=4)
     assert np.array_equal(c_ovl, c_plain)
-    assert done.cpu().tolist() == [mx.gemm_tiles_per_chunk(m, n, chunks)] * chunks == [256] * chunks
+    assert done.cpu().tolist() == [mx.gemm_tiles_per_chunk(m, n, chunks, 1, 1)] * chunks == [256] * chunks
     ref = oracle.gemm(qa, sa[1], 1, qb, sb[1], 1)
     _assert_close(c_ovl, ref, _abs_sum_full(qa, sa[1], 1, qb, sb[1], 1), f"split ring overlapped k={k}")
 
@@ -339,7 +339,7 @@ def test_gemm_two_group_256x192(kt):
     kernel. Ragged M and N tails (232 rows, 104 columns in the last tiles), each run after a
     decoy product: the same bits, and the oracle's at one K."""
     m, n, chunks, k = 1000, 12200, 1, 128 * kt
-    assert mx.gemm_tiles_per_chunk(m, n, chunks) == 4 * 64
+    assert mx.gemm_tiles_per_chunk(m, n, chunks, 1, 1) == 4 * 64
     print(f"two-group 256x192 k={k}", flush=True)
     qa, sa, qb, sb = _operands(m, n, k, seed_a=kt + 50, seed_b=kt + 51)
     xa, xsa, xb, xsb = _operands(m, n, k, seed_a=kt + 52, seed_b=kt + 53)
@@ -360,7 +360,7 @@ def test_gemm_two_group_256x192_two_tiles(kt):
     epilogue): the same bits as the staged kernel (rows 8 bytes off alignment), each run after a
     decoy product."""
     m, n, chunks, k = 2000, 12200, 2, 128 * kt
-    assert mx.gemm_tiles_per_chunk(m, n, chunks) == 4 * 64
+    assert mx.gemm_tiles_per_chunk(m, n, chunks, 1, 1) == 4 * 64
     print(f"two-group 256x192 two tiles k={k}", flush=True)
     qa, sa, qb, sb = _operands(m, n, k, seed_a=kt + 60, seed_b=kt + 61)
     xa, xsa, xb, xsb = _operands(m, n, k, seed_a=kt + 62, seed_b=kt + 63)
@@ -391,7 +391,7 @@ def test_gemm_chunk_counters_small_tiles():
     done = torch.zeros(4, dtype=torch.int32, device="cuda")
     c4 = _gpu_gemm(qa, sa[0], 0, qb, sb[0], 0, num_chunks=4, first_chunk=3, chunk_done=done)
     assert np.array_equal(c1, c4)
-    assert done.cpu().tolist() == [mx.gemm_tiles_per_chunk(m, n, 4)] * 4 == [48] * 4
+    assert done.cpu().tolist() == [mx.gemm_tiles_per_chunk(m, n, 4, 0, 0)] * 4 == [48] * 4
 
 
 def test_gemm_direct_tiles_count_and_match():
@@ -402,10 +402,10 @@ def test_gemm_direct_tiles_count_and_match():
     qa, sa, qb, sb = _operands(m + 108, n, k, seed_a=21, seed_b=22)
     done = torch.zeros(1, dtype=torch.int32, device="cuda")
     c = _gpu_gemm(qa[:m], sa[0][:m], 0, qb, sb[0], 0, num_chunks=1, chunk_done=done)
-    assert done.cpu().tolist() == [mx.gemm_tiles_per_chunk(m, n, 1)] == [192]
+    assert done.cpu().tolist() == [mx.gemm_tiles_per_chunk(m, n, 1, 0, 0)] == [192]
     ref = oracle.gemm(qa[:m], sa[0][:m], 0, qb, sb[0], 0)
     _assert_close(c, ref, _abs_sum_full(qa[:m], sa[0][:m], 0, qb, sb[0], 0), "direct tiles m=20")
-    assert mx.gemm_tiles_per_chunk(m + 108, n, 1) == 4 * 48
+    assert mx.gemm_tiles_per_chunk(m + 108, n, 1, 0, 0) == 4 * 48
     c_lds = _gpu_gemm(qa, sa[0], 0, qb, sb[0], 0, num_chunks=1)
     assert np.array_equal(c, c_lds[:m])
 
@@ -417,7 +417,7 @@ def test_gemm_chunking_is_bitwise_invariant():
     done = torch.zeros(4, dtype=torch.int32, device="cuda")
     c4 = _gpu_gemm(qa, sa[1], 1, qb, sb[1], 1, num_chunks=4, first_chunk=2, chunk_done=done)
     assert np.array_equal(c1, c4)
-    assert done.cpu().tolist() == [mx.gemm_tiles_per_chunk(m, n, 4)] * 4
+    assert done.cpu().tolist() == [mx.gemm_tiles_per_chunk(m, n, 4, 1, 1)] * 4
     c3 = _gpu_gemm(qa, sa[1], 1, qb, sb[1], 1, num_chunks=3, first_chunk=1)
     assert np.array_equal(c1, c3)
 
@@ -498,7 +498,7 @@ def test_gemm_wide_scale_range_split_ring():
     """The same on the 256 x 256 two-group kernel (swizzled, 16-byte aligned scales in
     registers), compared on sampled outputs."""
     m, n, k, chunks = 4096, 4096, 512, 4
-    assert mx.gemm_tiles_per_chunk(m, n, chunks) == 4 * 16
+    assert mx.gemm_tiles_per_chunk(m, n, chunks, 1, 1) == 4 * 16
     qa, sa, qb, sb = _wide_scale_operands(m, n, k, seed=11)
     c = _gpu_gemm(qa, sa[1], 1, qb, sb[1], 1, num_chunks=chunks)
     rng = np.random.default_rng(12)
@@ -530,7 +530,7 @@ def test_gemm_random_shapes_accum_bound(seed):
     the same absolute accumulation error)."""
     m, n, k, chunks, la, lb, first = _random_case(1000 + seed)
     print(f"gemm random seed={seed}: m={m} n={n} k={k} chunks={chunks} layouts={la}{lb} "
-          f"tiles/chunk={mx.gemm_tiles_per_chunk(m, n, chunks)}", flush=True)
+          f"tiles/chunk={mx.gemm_tiles_per_chunk(m, n, chunks, la, lb)}", flush=True)
     qa, sa, qb, sb = _operands(m, n, k, seed_a=3000 + seed, seed_b=4000 + seed)
     ref, exact = oracle.gemm(qa, sa[la], la, qb, sb[lb], lb, want_f64=True)
     c = _gpu_gemm(qa, sa[la], la, qb, sb[lb], lb, num_chunks=chunks, first_chunk=first)

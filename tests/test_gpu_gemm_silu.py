@@ -116,7 +116,7 @@ def test_gemm_silu_mul_quant_split_ring_matches_staged(m, inter, k, tile_n):
     cases, so workgroups take two or three); scale buffers 4 bytes off that alignment take the
     staged kernel. Both form the same fp32 sums, so codes and scales agree bit for bit (and with
     the oracle's within the accumulation bound, checked on the first case)."""
-    assert mx.gemm_tiles_per_chunk(m, 2 * inter, 1) == ((m + 255) // 256) * (2 * inter // tile_n)
+    assert mx.gemm_tiles_per_chunk(m, 2 * inter, 1, 1, 1) == ((m + 255) // 256) * (2 * inter // tile_n)
     print(f"fused GEMM1 two-group vs staged m={m} inter={inter} k={k}", flush=True)
     qa, sa, qw, sw = _operands(m, inter, k, seed_a=11, seed_w=12)
     outs = []
