@@ -55,8 +55,8 @@ def _parse():
 # counter of a 1 GiB copy onto 1 GiB. Valid only for the kernel code it was taken on
 # (gemm_code_sha256).
 GEMM_TRAFFIC = {
-    "source_sha256": "cfcfa873f8eecd7e4c84beeb6507e33015ad2fa03408e92d391dc60841b56e40",
-    "fetch_kib": 456989.6, "write_kib": 393301.5,
+    "source_sha256": "e6b96aea36e5a662e0b56db1d332fd69cfc18d062228c53482eb1b698d67f96e",
+    "fetch_kib": 457283.0, "write_kib": 393356.5,
     "fetch_factor": 2.0, "write_factor": 1.0,
 }
 
