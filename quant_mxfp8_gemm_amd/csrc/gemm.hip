@@ -686,8 +686,8 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
   }
 }
 
-// BF16-output GEMM on 256 x 256 or 256 x 192 tiles whose eight waves take turns on the matrix
-// pipes. Waves 0-3 (tile rows 0-127) and waves 4-7 (rows 128-255) put one wave of each group on
+// GEMM on 256 x 256 or 256 x 192 tiles whose eight waves take turns on the matrix pipes, with
+// BF16 output or the fused gate_up epilogue. Waves 0-3 (tile rows 0-127) and waves 4-7 (rows 128-255) put one wave of each group on
 // every SIMD. Each wave alternates a memory phase (the LDS fragment reads of one 64-K half step
 // into registers, then its share of the loads) and a compute phase (the half step's scaled
 // MFMAs from those registers), with a workgroup barrier after every phase; the second group
@@ -707,13 +707,15 @@ __global__ __launch_bounds__(T::NT, 1) void gemm_kernel(
 //    last barrier that precedes its first read and for A(s + 1) before the group's own first
 //    read. Loads past the last step go through empty resources (dropped) so that the counts
 //    hold on every path.
-//  * 256 x 256: after the last step of a tile the workgroup issues the next tile's B(0),
-//    scales, A(0) and B(1) (A slot 0, B slots 0 and 1), then writes the BF16 tile out in four
-//    quarters of 128 rows x 128 columns staged alternately in A slot 1 and B slot 2. The C
-//    stores are buffer stores over the tile's own rows (elements past the last row or column
-//    are dropped), so every wave issues the same 16 stores, and the next tile's first waits let
-//    exactly those stay in flight. 256 x 192 (two tiles per compute unit at most, for the
-//    M = 2048-4096 workloads): the whole tile is staged once the loads have landed.
+//  * 256 x 256, BF16: the next tile's B(0), scales, A(0) and B(1) (A slot 0, B slots 0 and 1)
+//    are issued by the tile's last two steps when its number of K steps is even (chained),
+//    else after its last step; then the tile leaves in four quarters of 128 rows x 128 columns
+//    staged alternately in A slot 1 and B slot 2. The C stores are buffer stores over the
+//    tile's own rows (elements past the last row or column are dropped), so every wave issues
+//    the same 16 stores, and the next tile's first waits let exactly those stay in flight.
+//    256 x 192 (two tiles per compute unit at most, for the M = 1536-4096 workloads) and the
+//    fused epilogue: the whole tile (fused: fp32 bands of it) is staged once every load has
+//    landed, then the next tile's first loads are issued.
 template <class T, int CH, int EPI = EPI_BF16>
 __global__ __launch_bounds__(T::NT, 1) void gemm_pingpong_bf16_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
